@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the DoRA module hot path on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch: the
+factored row norm, the base and adapter products, the fused compose
+(dora_forward) and the norm-detached backward (dora_backward), on the
+training-shaped module d_in 8192 -> d_out 28672, r 384, 8192 tokens, bf16
+(the shape and rank the Scaling-DoRA abstract works at).  Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.
+
+Printed JSON line (one):
+  value        module forward time per step (microseconds, HIP events), the
+               first quantity of the metric; ms_per_step covers forward +
+               backward, wall clock over the K timed steps.
+  compose_*    dora_compose alone, HBM GB/s with the 256 MB MALL flushed
+               before every launch (6 bytes per bf16 element).
+  norm_*       dora_factored_norm alone: algorithmic flops / time against
+               the 2.5 PFLOP/s dense bf16 MFMA peak.
+  roofline     the dominant kernel (the base product x W^T, bf16 MFMA),
+               timed with HIP events on the launch stream.
+  cpu_baseline the fp64 oracle forward on the same module on the host cores,
+               on a bounded token sample, extrapolated to the full batch.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DoRA module fwd µs + compose HBM GB/s + norm-GEMM MFMA util, r=384 bf16"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "base_gemm_traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """Hash of the GEMM kernel sources: counter readings are only reused for
+    the kernel they were taken on."""
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "epilogue.hpp", "dora_internal.hpp"):
+        with open(os.path.join(ROOT, "dora_adapter_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def norm_flops(d_out, d_in, r):
+    # U = W A^T, G = A A^T, B G (hi and lo), row sums of W^2, the two row dots
+    return 2 * d_out * d_in * r + 2 * r * r * d_in + 2 * 2 * d_out * r * r + 2 * d_out * d_in \
+        + 4 * d_out * r
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--leg", choices=["all", "step", "kernels", "base", "copy"], default="all",
+                    help="'base' launches only the dominant kernel (for counter runs); "
+                         "'copy' a plain device copy of known size (counter calibration)")
+    ap.add_argument("--iters", type=int, default=10, help="launches per kernel-leg timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the DoRA module path here has no multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dora_adapter_amd import dora as D
+    from dora_adapter_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    shape = synth.TRAIN_R384
+    T, d_in, d_out, r, s = shape.T, shape.d_in, shape.d_out, shape.r, shape.s
+
+    if args.leg == "copy":
+        nbytes = 1 << 30
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.iters):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "launches": args.iters}))
+        return
+
+    log("generating", shape.name)
+    mod = synth.make_module(shape, seed=0, with_dy=True)
+    t = {k: mod[k].to(dev) for k in ("x", "W", "A", "B", "m", "dy")}
+    del mod
+    torch.cuda.synchronize()
+
+    if args.leg == "base":
+        y = torch.empty(T, d_out, dtype=torch.bfloat16, device=dev)
+        for _ in range(args.iters):
+            D.dora_linear(t["x"], t["W"], y=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "base", "launches": args.iters,
+                          "flops_per_launch": 2 * T * d_in * d_out}))
+        return
+
+    # Preallocated outputs and workspaces: nothing is allocated inside the step.
+    y = torch.empty(T, d_out, dtype=torch.bfloat16, device=dev)
+    n = torch.empty(d_out, dtype=torch.float32, device=dev)
+    P = torch.empty(T, r, dtype=torch.bfloat16, device=dev)
+    grads = {"dx": torch.empty(T, d_in, dtype=torch.bfloat16, device=dev),
+             "dA": torch.empty(r, d_in, dtype=torch.bfloat16, device=dev),
+             "dB": torch.empty(d_out, r, dtype=torch.bfloat16, device=dev),
+             "dm": torch.empty(d_out, dtype=torch.float32, device=dev)}
+    ws_f = torch.empty(D.dora_forward_workspace(T, d_in, d_out, r, 1), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(D.dora_backward_workspace(T, d_in, d_out, r, 1), dtype=torch.uint8,
+                       device=dev)
+
+    def fwd():
+        D.dora_forward(t["x"], t["W"], t["A"], t["B"], t["m"], s, ws=ws_f, y=y, n_out=n, P_out=P)
+
+    def bwd():
+        D.dora_backward(t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P, y, ws=ws_b,
+                        out=grads)
+
+    out = {"metric": METRIC, "unit": "µs", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; W, A ~ N(0, 1/d_in), B ~ N(0, 0.02^2), "
+                   "m = ||W_i|| (1 + N(0, 0.01^2)), x, dy ~ N(0, 1))",
+           "config": {"workload": shape.name, "d_in": d_in, "d_out": d_out, "r": r,
+                      "tokens": T, "s": s,
+                      "step": "factored norm + forward + compose + norm-detached backward",
+                      "parallelism": "single GPU"}}
+
+    if args.leg in ("all", "step"):
+        log(f"warmup {args.warmup}")
+        for _ in range(args.warmup):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        log(f"timing {args.steps} steps")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            ev[k][0].record()
+            fwd()
+            ev[k][1].record()
+            bwd()
+            ev[k][2].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        fwd_us = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e3
+        bwd_us = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e3
+        out.update(value=round(fwd_us, 1), ms_per_step=round((t1 - t0) / args.steps * 1e3, 3),
+                   fwd_us=round(fwd_us, 1), bwd_us=round(bwd_us, 1),
+                   fwd_tflops=round((2 * T * d_in * d_out + 2 * T * r * (d_in + d_out)
+                                     + norm_flops(d_out, d_in, r)) / fwd_us / 1e6, 1),
+                   bwd_tflops=round((2 * T * d_out * d_in + 4 * T * d_out * r + 4 * T * r * d_in)
+                                    / bwd_us / 1e6, 1))
+        log(f"fwd {fwd_us:.1f} us  bwd {bwd_us:.1f} us")
+
+    if args.leg in ("all", "kernels"):
+        def timed(fn, pre=None):
+            tot = 0.0
+            for _ in range(2):
+                fn()
+            for _ in range(args.iters):
+                if pre is not None:
+                    pre()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                b.synchronize()
+                tot += a.elapsed_time(b)
+            return tot / args.iters * 1e3
+
+        # dominant kernel: the base product x W^T (one launch of the bf16 MFMA GEMM)
+        y_lin = torch.empty_like(y)
+        base_us = timed(lambda: D.dora_linear(t["x"], t["W"], y=y_lin))
+        flops = 2 * T * d_in * d_out
+        ach = flops / base_us / 1e6
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as fh:
+                tr = json.load(fh)
+            if tr.get("kernel_source_hash") == kernel_source_hash():
+                traffic = tr.get("hbm_bytes_per_launch")
+        out["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic, "kernel": "gemm_bf16 x W^T (dora_linear)",
+                           "flops_per_launch": flops, "us_per_launch": round(base_us, 1)}
+        log(f"base GEMM {base_us:.1f} us = {ach:.0f} TFLOP/s")
+
+        ws_n = torch.empty(D.dora_norm_workspace(d_out, d_in, r, 1), dtype=torch.uint8,
+                           device=dev)
+        n2 = torch.empty_like(n)
+        norm_us = timed(lambda: D.dora_factored_norm(t["W"], t["A"], t["B"], s, ws=ws_n, n=n2))
+        nf = norm_flops(d_out, d_in, r)
+        out["norm_us"] = round(norm_us, 1)
+        out["norm_mfma_util"] = round(nf / norm_us / 1e6 / PEAK_BF16_TFLOPS, 4)
+        log(f"norm {norm_us:.1f} us = {nf / norm_us / 1e6:.0f} TFLOP/s")
+
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        lora = torch.randn(T, d_out, device=dev).bfloat16()
+        yc = torch.empty_like(y)
+        comp_us = timed(lambda: D.dora_compose(y, lora, t["m"], n, s, y=yc),
+                        pre=lambda: flush.fill_(1))
+        gbps = 6 * T * d_out / comp_us / 1e3
+        out["compose_us"] = round(comp_us, 1)
+        out["compose_GBps"] = round(gbps, 1)
+        out["compose_frac_hbm"] = round(gbps / PEAK_HBM_GBPS, 4)
+        log(f"compose {comp_us:.1f} us = {gbps:.0f} GB/s (MALL flushed)")
+        del flush, lora, yc, y_lin
+
+    if args.leg == "all" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(t, shape)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(t, shape):
+    """The fp64 oracle's forward on the same module, on the host cores.  Its
+    cost is a per-row part (forming row i of W + sBA: d_in * r) plus a
+    per-token part (d_in per row); two token counts give both, and the time
+    is extrapolated linearly to the full token count."""
+    from oracle import oracle as O
+    cpu = {k: t[k].cpu() for k in ("x", "W", "A", "B", "m")}
+    times = {}
+    for ntok in (8, 136):
+        toks = list(range(ntok))
+        log(f"cpu baseline: oracle forward on {ntok} tokens")
+        a = time.perf_counter()
+        O.forward(cpu["x"], cpu["W"], cpu["A"], cpu["B"], cpu["m"], shape.s, toks=toks)
+        times[ntok] = time.perf_counter() - a
+    per_tok = (times[136] - times[8]) / 128
+    fixed = times[8] - 8 * per_tok
+    full_s = fixed + per_tok * shape.T
+    return {"value": round(full_s * 1e6, 0), "unit": "µs", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"oracle forward (fp64, dense W + sBA rows) at the full module shape on "
+                      f"8 and 136 tokens ({times[8]:.1f} s, {times[136]:.1f} s); fixed + per-token "
+                      f"cost extrapolated to {shape.T} tokens"}
+
+
+if __name__ == "__main__":
+    main()

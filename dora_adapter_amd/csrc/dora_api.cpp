@@ -1,0 +1,648 @@
+// dora_api.cpp - the C ABI of libdora.so (declared in include/dora.h).
+//
+// Host-side only: argument validation (before anything is enqueued), the
+// launch plan (tile shape and split-K per product), the workspace carve-up
+// and the launch sequences of the factored norm, the compose, the forward
+// and the norm-detached backward.  Every step of the computation runs in
+// the HIP kernels of gemm_bf16.hip, gemm_f32.hip and elementwise.hip.
+#include <stdio.h>
+#include <stdarg.h>
+#include <string.h>
+
+#include <algorithm>
+#include <initializer_list>
+
+#include "../../include/dora.h"
+#include "dora_internal.hpp"
+
+namespace dora {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(DORA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DORA_LAUNCH(expr, what)                      \
+    do {                                             \
+        hipError_t e_ = (expr);                      \
+        if (e_ != hipSuccess)                        \
+            return hip_fail(e_, what);               \
+    } while (0)
+
+constexpr int64_t kMaxDim = (1LL << 31) - 1;
+constexpr size_t kAlign = 256;
+constexpr int kCUs = 256;
+
+size_t esize(int dtype) { return dtype == DORA_BF16 ? 2 : 4; }
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ------------------------------------------------------------------ planning
+struct GPlan {
+    int cfg = 0;         // bf16 tile shape index (fp32: unused)
+    int BM = 0, BN = 0;
+    int splits = 1;
+    int64_t sps = 0;     // K steps per split
+    int ntn = 0;         // tiles along N
+};
+
+// Choose the tile shape and the split-K count for C[M, N] over `steps`
+// K steps by a small time model: (256-CU waves) x (one workgroup's MFMA or
+// VALU time), plus, for a split, writing and re-reading `part_per_split`
+// fp32 values per split and one extra launch.  A split must keep at least
+// 8 K steps and its partials under 1 GiB.
+GPlan plan_gemm(bool bf16, int64_t M, int64_t N, int64_t steps, int64_t part_per_split)
+{
+    const double cu_flops = bf16 ? 2.5e15 / kCUs * 0.7 : 157.3e12 / kCUs * 0.5;
+    const double hbm = 5.0e12;
+    const int64_t bk = bf16 ? GEMM_BK : GEMM_F32_BK;
+    GPlan best;
+    double best_cost = -1.0;
+    const int ncfg = bf16 ? gemm_bf16_num_cfgs() : 1;
+    for (int c = 0; c < ncfg; ++c) {
+        int BM, BN;
+        float rel;
+        if (bf16) {
+            TileCfg t = gemm_bf16_cfg(c);
+            BM = t.BM;
+            BN = t.BN;
+            rel = t.rel_speed;
+        } else {
+            BM = GEMM_F32_BM;
+            BN = GEMM_F32_BN;
+            rel = 1.0f;
+        }
+        const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        const int64_t zmax = std::min<int64_t>(32, std::max<int64_t>(steps / 8, 1));
+        for (int64_t z = 1; z <= zmax; ++z) {
+            if (z > 1 && static_cast<double>(z) * part_per_split * 4.0 > (1LL << 30))
+                break;
+            const int64_t sps = (steps + z - 1) / z;
+            const int64_t waves = std::max<int64_t>((tiles * z + kCUs - 1) / kCUs, 1);
+            double cost = static_cast<double>(waves) * 2.0 * BM * BN * bk *
+                          static_cast<double>(std::max<int64_t>(sps, 1)) / (cu_flops * rel);
+            if (z > 1)
+                cost += 2.0 * z * part_per_split * 4.0 / hbm + 3e-6;
+            if (best_cost < 0 || cost < best_cost * 0.97) {
+                best_cost = cost;
+                best.cfg = c;
+                best.BM = BM;
+                best.BN = BN;
+                best.splits = static_cast<int>(z);
+                best.sps = sps;
+                best.ntn = static_cast<int>((N + BN - 1) / BN);
+            }
+        }
+    }
+    return best;
+}
+
+int64_t ksteps(bool bf16, int64_t K)
+{
+    const int64_t bk = bf16 ? GEMM_BK : GEMM_F32_BK;
+    return (K + bk - 1) / bk;
+}
+
+// Workspace carve-up: offsets are computed identically by the size queries
+// and by the calls.
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes)
+    {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    }
+};
+
+struct NormPlan {
+    GPlan g, u, bg;
+    size_t o_gpart, o_gfin, o_base, o_cross, o_gram;
+    size_t bytes;
+};
+
+NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, Carve &cv)
+{
+    const bool bf = dtype == DORA_BF16;
+    NormPlan p;
+    p.g = plan_gemm(bf, r, r, ksteps(bf, d_in), r * r);
+    p.u = plan_gemm(bf, d_out, r, ksteps(bf, d_in), 2 * d_out);
+    p.bg = plan_gemm(bf, d_out, r, (bf ? 2 : 1) * ksteps(bf, r), d_out);
+    const size_t start = cv.off;
+    p.o_gpart = cv.take(static_cast<size_t>(p.g.splits) * r * r * 4);
+    p.o_gfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);
+    p.o_base = cv.take(static_cast<size_t>(p.u.splits) * d_out * 4);
+    p.o_cross = cv.take(static_cast<size_t>(p.u.splits) * p.u.ntn * d_out * 4);
+    p.o_gram = cv.take(static_cast<size_t>(p.bg.splits) * p.bg.ntn * d_out * 4);
+    p.bytes = cv.off - start;
+    return p;
+}
+
+struct LinPlan {
+    GPlan g;
+    size_t bytes;
+};
+
+// The base product's plan, shared by dora_forward and dora_linear.
+GPlan plan_base(bool bf, int64_t T, int64_t d_in, int64_t d_out)
+{
+    return plan_gemm(bf, T, d_out, ksteps(bf, d_in), T * d_out);
+}
+
+LinPlan plan_linear(int64_t T, int64_t d_in, int64_t d_out, int dtype)
+{
+    LinPlan l;
+    l.g = plan_base(dtype == DORA_BF16, T, d_in, d_out);
+    l.bytes = l.g.splits > 1 ? align_up(static_cast<size_t>(l.g.splits) * T * d_out * 4) : 0;
+    return l;
+}
+
+struct FwdPlan {
+    NormPlan norm;
+    GPlan base, p, lora;
+    size_t o_P, o_Ppart, o_lora, o_part_lora, o_part_base;
+    size_t bytes;
+};
+
+FwdPlan plan_forward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype)
+{
+    const bool bf = dtype == DORA_BF16;
+    FwdPlan f;
+    Carve cv;
+    f.norm = plan_norm(d_out, d_in, r, dtype, cv);
+    f.base = plan_base(bf, T, d_in, d_out);
+    f.p = plan_gemm(bf, T, r, ksteps(bf, d_in), T * r);
+    f.lora = plan_gemm(bf, T, d_out, ksteps(bf, r), T * d_out);
+    const size_t e = esize(dtype);
+    f.o_P = cv.take(static_cast<size_t>(T) * r * e);
+    f.o_Ppart = cv.take(f.p.splits > 1 ? static_cast<size_t>(f.p.splits) * T * r * 4 : 0);
+    f.o_lora = cv.take(static_cast<size_t>(T) * d_out * e);
+    f.o_part_lora =
+        cv.take(f.lora.splits > 1 ? static_cast<size_t>(f.lora.splits) * T * d_out * 4 : 0);
+    f.o_part_base =
+        cv.take(f.base.splits > 1 ? static_cast<size_t>(f.base.splits) * T * d_out * 4 : 0);
+    f.bytes = cv.off;
+    return f;
+}
+
+struct BwdPlan {
+    GPlan q, dx, dB, dA;
+    int64_t t_chunk;
+    int nchunks;
+    size_t o_dh, o_dmpart, o_Q, o_Qpart, o_dxpart, o_dBpart, o_dApart;
+    size_t bytes;
+};
+
+BwdPlan plan_backward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype)
+{
+    const bool bf = dtype == DORA_BF16;
+    BwdPlan b;
+    Carve cv;
+    b.q = plan_gemm(bf, T, r, ksteps(bf, d_out), T * r);
+    b.dx = plan_gemm(bf, T, d_in, ksteps(bf, d_out) + ksteps(bf, r), T * d_in);
+    b.dB = plan_gemm(bf, d_out, r, ksteps(bf, T), d_out * r);
+    b.dA = plan_gemm(bf, r, d_in, ksteps(bf, T), r * d_in);
+    b.t_chunk = dm_t_chunk(T, d_out);
+    b.nchunks = T > 0 ? static_cast<int>((T + b.t_chunk - 1) / b.t_chunk) : 0;
+    const size_t e = esize(dtype);
+    b.o_dh = cv.take(static_cast<size_t>(T) * d_out * e);
+    b.o_dmpart = cv.take(static_cast<size_t>(std::max(b.nchunks, 1)) * d_out * 4);
+    b.o_Q = cv.take(static_cast<size_t>(T) * r * e);
+    b.o_Qpart = cv.take(b.q.splits > 1 ? static_cast<size_t>(b.q.splits) * T * r * 4 : 0);
+    b.o_dxpart = cv.take(b.dx.splits > 1 ? static_cast<size_t>(b.dx.splits) * T * d_in * 4 : 0);
+    b.o_dBpart = cv.take(b.dB.splits > 1 ? static_cast<size_t>(b.dB.splits) * d_out * r * 4 : 0);
+    b.o_dApart = cv.take(b.dA.splits > 1 ? static_cast<size_t>(b.dA.splits) * r * d_in * 4 : 0);
+    b.bytes = cv.off;
+    return b;
+}
+
+// ---------------------------------------------------------------- validation
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(Range a, Range b)
+{
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0)
+        return false;
+    const char *a0 = static_cast<const char *>(a.p), *b0 = static_cast<const char *>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_dtype(int dtype)
+{
+    if (dtype != DORA_F32 && dtype != DORA_BF16)
+        return fail(DORA_E_DTYPE, "unknown dtype %d", dtype);
+    return DORA_OK;
+}
+
+int check_dims(int dtype, int64_t T, int64_t d_in, int64_t d_out, int64_t r)
+{
+    if (T < 0 || T > kMaxDim)
+        return fail(DORA_E_SHAPE, "T=%lld out of range [0, 2^31)", (long long)T);
+    if (d_in < 1 || d_in > kMaxDim || d_out < 1 || d_out > kMaxDim || r < 1 || r > kMaxDim)
+        return fail(DORA_E_SHAPE, "need 1 <= d_in, d_out, r < 2^31 (got %lld, %lld, %lld)",
+                    (long long)d_in, (long long)d_out, (long long)r);
+    if (dtype == DORA_BF16 && ((d_in % 8) || (d_out % 8) || (r % 8)))
+        return fail(DORA_E_SHAPE, "bf16 needs d_in, d_out, r multiples of 8 (got %lld, %lld, %lld)",
+                    (long long)d_in, (long long)d_out, (long long)r);
+    return DORA_OK;
+}
+
+struct Ptr {
+    const void *p;
+    const char *name;
+    bool required;
+};
+
+int check_ptrs(std::initializer_list<Ptr> ps)
+{
+    for (const Ptr &q : ps) {
+        if (!q.p) {
+            if (q.required)
+                return fail(DORA_E_NULL, "%s is NULL", q.name);
+            continue;
+        }
+        if (!aligned(q.p))
+            return fail(DORA_E_ALIGN, "%s is not 16-byte aligned", q.name);
+    }
+    return DORA_OK;
+}
+
+int check_ws(void *ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0)
+        return DORA_OK;
+    if (!ws)
+        return fail(DORA_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (ws_bytes < need)
+        return fail(DORA_E_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned(ws))
+        return fail(DORA_E_ALIGN, "workspace is not 16-byte aligned");
+    return DORA_OK;
+}
+
+struct Named {
+    Range r;
+    const char *name;
+};
+
+// Every output must be disjoint from every other listed buffer.
+int check_disjoint(std::initializer_list<Named> outs, std::initializer_list<Named> others)
+{
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(o->r, o2->r))
+                return fail(DORA_E_ALIAS, "%s overlaps %s", o->name, o2->name);
+        for (const Named &b : others)
+            if (overlap(o->r, b.r))
+                return fail(DORA_E_ALIAS, "%s overlaps %s", o->name, b.name);
+    }
+    return DORA_OK;
+}
+
+#define DORA_CHECK(expr)             \
+    do {                             \
+        int rc_ = (expr);            \
+        if (rc_ != DORA_OK)          \
+            return rc_;              \
+    } while (0)
+
+// ----------------------------------------------------------------- launching
+hipError_t run_gemm(bool bf16, const GPlan &p, GemmArgs a, int layout, bool rowsq, hipStream_t st)
+{
+    a.splits = p.splits;
+    a.steps_per_split = p.sps;
+    return bf16 ? launch_gemm_bf16(a, layout, p.cfg, rowsq, st)
+                : launch_gemm_f32(a, layout, rowsq, st);
+}
+
+GemmArgs seg1(int64_t M, int64_t N, const void *a, int64_t lda, const void *b, int64_t ldb,
+              int64_t K)
+{
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.M = M;
+    g.N = N;
+    g.seg[0] = GemmSeg{a, lda, b, ldb, K};
+    g.nseg = 1;
+    g.alpha = 1.0f;
+    return g;
+}
+
+// A store-mode product: directly into `out` (dtype) when unsplit, otherwise
+// through fp32 split partials and a fixed-order reduction.
+int run_store(bool bf16, const GPlan &p, GemmArgs a, int layout, void *out, int64_t ldc,
+              float alpha, float *part, hipStream_t st, const char *what)
+{
+    a.mode = EPI_STORE;
+    if (p.splits <= 1) {
+        a.out = out;
+        a.ldc = ldc;
+        a.out_f32 = bf16 ? 0 : 1;
+        a.alpha = alpha;
+        DORA_LAUNCH(run_gemm(bf16, p, a, layout, false, st), what);
+    } else {
+        a.out = part;
+        a.ldc = a.N;
+        a.out_f32 = 1;
+        a.alpha = 1.0f;
+        DORA_LAUNCH(run_gemm(bf16, p, a, layout, false, st), what);
+        DORA_LAUNCH(launch_splitk_reduce(bf16, part, p.splits, a.M, a.N, alpha, out, st), what);
+    }
+    return DORA_OK;
+}
+
+int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_out, int64_t d_in,
+              int64_t r, int dtype, float *n, float *base, float *cross, float *gram,
+              const NormPlan &p, char *ws, hipStream_t st)
+{
+    const bool bf = dtype == DORA_BF16;
+    float *gpart = reinterpret_cast<float *>(ws + p.o_gpart);
+    void *gfin = ws + p.o_gfin;
+    float *bpart = reinterpret_cast<float *>(ws + p.o_base);
+    float *cpart = reinterpret_cast<float *>(ws + p.o_cross);
+    float *gmpart = reinterpret_cast<float *>(ws + p.o_gram);
+
+    // G = A A^T, split-K partials, then a fixed-order sum (+ hi/lo split for bf16).
+    {
+        GemmArgs g = seg1(r, r, A, d_in, A, d_in, d_in);
+        g.mode = EPI_STORE;
+        g.out = gpart;
+        g.ldc = r;
+        g.out_f32 = 1;
+        DORA_LAUNCH(run_gemm(bf, p.g, g, 0, false, st), "gram A A^T");
+        DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, gfin, st), "gram finalize");
+    }
+    // U = W A^T never leaves the tile: cross partials = rowdot(U_tile, B_tile),
+    // base partials = row sums of W^2 from the same staged W.
+    {
+        GemmArgs g = seg1(d_out, r, W, d_in, A, d_in, d_in);
+        g.mode = EPI_ROWDOT;
+        g.E = B;
+        g.lde = r;
+        g.rowdot = cpart;
+        g.rowsq = bpart;
+        DORA_LAUNCH(run_gemm(bf, p.u, g, 0, true, st), "cross W A^T");
+    }
+    // gram partials = rowdot(B G, B); bf16 forms B G as B G_hi + B G_lo.
+    {
+        GemmArgs g = seg1(d_out, r, B, r, gfin, r, r);
+        if (bf) {
+            g.seg[1] = GemmSeg{B, r, static_cast<const uint16_t *>(gfin) + r * r, r, r};
+            g.nseg = 2;
+        }
+        g.mode = EPI_ROWDOT;
+        g.E = B;
+        g.lde = r;
+        g.rowdot = gmpart;
+        DORA_LAUNCH(run_gemm(bf, p.bg, g, 1, false, st), "gram B G");
+    }
+    DORA_LAUNCH(launch_norm_finish(bpart, p.u.splits, cpart, p.u.splits * p.u.ntn, gmpart,
+                                   p.bg.splits * p.bg.ntn, d_out, s, n, base, cross, gram, st),
+                "norm finish");
+    return DORA_OK;
+}
+
+}  // namespace
+}  // namespace dora
+
+using namespace dora;
+
+extern "C" {
+
+const char *dora_strerror(int status)
+{
+    switch (status) {
+    case DORA_OK: return "ok";
+    case DORA_E_NULL: return "required pointer is NULL";
+    case DORA_E_SHAPE: return "invalid shape";
+    case DORA_E_DTYPE: return "invalid dtype";
+    case DORA_E_ALIGN: return "pointer not 16-byte aligned";
+    case DORA_E_WORKSPACE: return "workspace missing or too small";
+    case DORA_E_ALIAS: return "buffers overlap";
+    case DORA_E_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *dora_last_error(void) { return g_last_error; }
+
+size_t dora_norm_workspace(int64_t d_out, int64_t d_in, int64_t r, int dtype)
+{
+    if (check_dtype(dtype) || check_dims(dtype, 0, d_in, d_out, r))
+        return 0;
+    Carve cv;
+    return plan_norm(d_out, d_in, r, dtype, cv).bytes;
+}
+
+size_t dora_forward_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype)
+{
+    if (check_dtype(dtype) || check_dims(dtype, T, d_in, d_out, r))
+        return 0;
+    return plan_forward(T, d_in, d_out, r, dtype).bytes;
+}
+
+size_t dora_backward_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype)
+{
+    if (check_dtype(dtype) || check_dims(dtype, T, d_in, d_out, r))
+        return 0;
+    return plan_backward(T, d_in, d_out, r, dtype).bytes;
+}
+
+int dora_factored_norm(const void *W, const void *A, const void *B, float s, int64_t d_out,
+                       int64_t d_in, int64_t r, int dtype, float *n, float *base, float *cross,
+                       float *gram, void *ws, size_t ws_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_dims(dtype, 0, d_in, d_out, r));
+    DORA_CHECK(check_ptrs({{W, "W", true}, {A, "A", true}, {B, "B", true}, {n, "n", true},
+                           {base, "base", false}, {cross, "cross", false}, {gram, "gram", false}}));
+    Carve cv;
+    const NormPlan p = plan_norm(d_out, d_in, r, dtype, cv);
+    DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
+    const size_t e = esize(dtype);
+    const Range rW{W, d_out * d_in * e}, rA{A, r * d_in * e}, rB{B, d_out * r * e};
+    const Range rws{ws, p.bytes};
+    const size_t v = d_out * 4;
+    DORA_CHECK(check_disjoint({{{n, v}, "n"}, {{base, v}, "base"}, {{cross, v}, "cross"},
+                               {{gram, v}, "gram"}, {rws, "workspace"}},
+                              {{rW, "W"}, {rA, "A"}, {rB, "B"}}));
+    return norm_impl(W, A, B, s, d_out, d_in, r, dtype, n, base, cross, gram, p,
+                     static_cast<char *>(ws), static_cast<hipStream_t>(stream));
+}
+
+int dora_compose(const void *base, const void *lora, const float *m, const float *n, float s,
+                 int64_t T, int64_t d_out, int dtype, void *y, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    if (T < 0 || T > kMaxDim || d_out < 0 || d_out > kMaxDim)
+        return fail(DORA_E_SHAPE, "T=%lld, d_out=%lld out of range", (long long)T,
+                    (long long)d_out);
+    if (dtype == DORA_BF16 && (d_out % 8))
+        return fail(DORA_E_SHAPE, "bf16 needs d_out a multiple of 8 (got %lld)", (long long)d_out);
+    const bool any = T > 0 && d_out > 0;  // empty tensors may come with NULL data
+    DORA_CHECK(check_ptrs({{base, "base", any}, {lora, "lora", any}, {m, "m", d_out > 0},
+                           {n, "n", d_out > 0}, {y, "y", any}}));
+    const size_t bytes = static_cast<size_t>(T) * d_out * esize(dtype);
+    if (y != base && overlap({y, bytes}, {base, bytes}))
+        return fail(DORA_E_ALIAS, "y partially overlaps base");
+    DORA_CHECK(check_disjoint({{{y, bytes}, "y"}},
+                              {{{lora, bytes}, "lora"}, {{m, d_out * sizeof(float)}, "m"},
+                               {{n, d_out * sizeof(float)}, "n"}}));
+    DORA_LAUNCH(launch_compose(dtype == DORA_BF16, base, lora, m, n, s, T, d_out, y,
+                               static_cast<hipStream_t>(stream)),
+                "compose");
+    return DORA_OK;
+}
+
+int dora_forward(const void *x, const void *W, const void *A, const void *B, const float *m,
+                 float s, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype, void *y,
+                 float *n_out, void *P_out, const float *n_in, void *ws, size_t ws_bytes,
+                 void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_dims(dtype, T, d_in, d_out, r));
+    const bool has_t = T > 0;  // empty tensors may come with NULL data
+    DORA_CHECK(check_ptrs({{x, "x", has_t}, {W, "W", true}, {A, "A", true}, {B, "B", true},
+                           {m, "m", true}, {y, "y", has_t}, {n_out, "n_out", true},
+                           {P_out, "P_out", false}, {n_in, "n_in", false}}));
+    const FwdPlan p = plan_forward(T, d_in, d_out, r, dtype);
+    DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
+    const bool bf = dtype == DORA_BF16;
+    const size_t e = esize(dtype);
+    const Range rx{x, T * d_in * e}, rW{W, d_out * d_in * e}, rA{A, r * d_in * e},
+        rB{B, d_out * r * e}, rm{m, d_out * sizeof(float)}, rnin{n_in, d_out * sizeof(float)};
+    const Range ry{y, T * d_out * e}, rn{n_out, d_out * sizeof(float)}, rP{P_out, T * r * e}, rws{ws, p.bytes};
+    if (n_in && n_in != n_out && overlap(rn, rnin))
+        return fail(DORA_E_ALIAS, "n_out partially overlaps n_in");
+    DORA_CHECK(check_disjoint({{ry, "y"}, {rn, "n_out"}, {rP, "P_out"}, {rws, "workspace"}},
+                              {{rx, "x"}, {rW, "W"}, {rA, "A"}, {rB, "B"}, {rm, "m"}}));
+    DORA_CHECK(check_disjoint({{ry, "y"}, {rP, "P_out"}, {rws, "workspace"}}, {{rnin, "n_in"}}));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    // 1. the row norm (factored), unless the caller has it.
+    if (n_in) {
+        if (n_in != n_out)
+            DORA_LAUNCH(launch_copy_f32(n_in, n_out, d_out, st), "copy n_in");
+    } else {
+        DORA_CHECK(norm_impl(W, A, B, s, d_out, d_in, r, dtype, n_out, nullptr, nullptr, nullptr,
+                             p.norm, w, st));
+    }
+    if (T == 0)
+        return DORA_OK;
+    void *P = P_out ? P_out : static_cast<void *>(w + p.o_P);
+    void *lora = w + p.o_lora;
+    // 2. base = x W^T, written straight into y.
+    DORA_CHECK(run_store(bf, p.base, seg1(T, d_out, x, d_in, W, d_in, d_in), 0, y, d_out, 1.0f,
+                         reinterpret_cast<float *>(w + p.o_part_base), st, "base x W^T"));
+    // 3. P = x A^T.
+    DORA_CHECK(run_store(bf, p.p, seg1(T, r, x, d_in, A, d_in, d_in), 0, P, r, 1.0f,
+                         reinterpret_cast<float *>(w + p.o_Ppart), st, "adapter x A^T"));
+    // 4. lora = P B^T.
+    DORA_CHECK(run_store(bf, p.lora, seg1(T, d_out, P, r, B, r, r), 0, lora, d_out, 1.0f,
+                         reinterpret_cast<float *>(w + p.o_part_lora), st, "adapter P B^T"));
+    // 5. y = compose(base, lora) in place.
+    DORA_LAUNCH(launch_compose(bf, y, lora, m, n_out, s, T, d_out, y, st), "compose");
+    return DORA_OK;
+}
+
+int dora_backward(const void *dy, const void *x, const void *W, const void *A, const void *B,
+                  const float *m, const float *n, float s, const void *P, const void *y,
+                  int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype, void *dx, void *dA,
+                  void *dB, float *dm, void *ws, size_t ws_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_dims(dtype, T, d_in, d_out, r));
+    const bool has_t = T > 0;
+    DORA_CHECK(check_ptrs({{dy, "dy", has_t}, {x, "x", has_t}, {W, "W", true}, {A, "A", true},
+                           {B, "B", true}, {m, "m", true}, {n, "n", true}, {P, "P", has_t},
+                           {y, "y", has_t}, {dx, "dx", has_t}, {dA, "dA", true}, {dB, "dB", true},
+                           {dm, "dm", true}}));
+    const BwdPlan p = plan_backward(T, d_in, d_out, r, dtype);
+    DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
+    const bool bf = dtype == DORA_BF16;
+    const size_t e = esize(dtype);
+    DORA_CHECK(check_disjoint(
+        {{{dx, T * d_in * e}, "dx"}, {{dA, r * d_in * e}, "dA"}, {{dB, d_out * r * e}, "dB"},
+         {{dm, d_out * sizeof(float)}, "dm"}, {{ws, p.bytes}, "workspace"}},
+        {{{dy, T * d_out * e}, "dy"}, {{x, T * d_in * e}, "x"}, {{W, d_out * d_in * e}, "W"},
+         {{A, r * d_in * e}, "A"}, {{B, d_out * r * e}, "B"}, {{m, d_out * sizeof(float)}, "m"},
+         {{n, d_out * sizeof(float)}, "n"}, {{P, T * r * e}, "P"}, {{y, T * d_out * e}, "y"}}));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    void *dh = w + p.o_dh;
+    float *dmpart = reinterpret_cast<float *>(w + p.o_dmpart);
+    void *Q = w + p.o_Q;
+
+    // 1. dh = g dy and dm partial sums (one pass over dy and y), then dm.
+    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, p.t_chunk, dh, dmpart, st), "dh/dm");
+    DORA_LAUNCH(launch_dm_finish(dmpart, p.nchunks, m, d_out, dm, st), "dm finish");
+    // 2. Q = s dh B  (A K-major, B MN-major).
+    DORA_CHECK(run_store(bf, p.q, seg1(T, r, dh, d_out, B, r, d_out), 1, Q, r, s,
+                         reinterpret_cast<float *>(w + p.o_Qpart), st, "Q = s dh B"));
+    // 3. dx = [dh | Q] [W ; A]  (K-concatenated segments, B MN-major).
+    {
+        GemmArgs g = seg1(T, d_in, dh, d_out, W, d_in, d_out);
+        g.seg[1] = GemmSeg{Q, r, A, d_in, r};
+        g.nseg = 2;
+        DORA_CHECK(run_store(bf, p.dx, g, 1, dx, d_in, 1.0f,
+                             reinterpret_cast<float *>(w + p.o_dxpart), st, "dx"));
+    }
+    // 4. dB = s dh^T P  (both MN-major, K = T).
+    DORA_CHECK(run_store(bf, p.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, dB, r, s,
+                         reinterpret_cast<float *>(w + p.o_dBpart), st, "dB"));
+    // 5. dA = Q^T x  (both MN-major, K = T).
+    DORA_CHECK(run_store(bf, p.dA, seg1(r, d_in, Q, r, x, d_in, T), 2, dA, d_in, 1.0f,
+                         reinterpret_cast<float *>(w + p.o_dApart), st, "dA"));
+    return DORA_OK;
+}
+
+size_t dora_linear_workspace(int64_t T, int64_t d_in, int64_t d_out, int dtype)
+{
+    if (check_dtype(dtype) || check_dims(dtype, T, d_in, d_out, 8))
+        return 0;
+    return plan_linear(T, d_in, d_out, dtype).bytes;
+}
+
+int dora_linear(const void *x, const void *W, int64_t T, int64_t d_in, int64_t d_out, int dtype,
+                void *y, void *ws, size_t ws_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_dims(dtype, T, d_in, d_out, 8));
+    const bool has_t = T > 0;
+    DORA_CHECK(check_ptrs({{x, "x", has_t}, {W, "W", true}, {y, "y", has_t}}));
+    const LinPlan p = plan_linear(T, d_in, d_out, dtype);
+    DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
+    const size_t e = esize(dtype);
+    DORA_CHECK(check_disjoint({{{y, T * d_out * e}, "y"}, {{ws, p.bytes}, "workspace"}},
+                              {{{x, T * d_in * e}, "x"}, {{W, d_out * d_in * e}, "W"}}));
+    if (T == 0)
+        return DORA_OK;
+    return run_store(dtype == DORA_BF16, p.g, seg1(T, d_out, x, d_in, W, d_in, d_in), 0, y, d_out,
+                     1.0f, static_cast<float *>(ws), static_cast<hipStream_t>(stream),
+                     "linear x W^T");
+}
+
+}  // extern "C"

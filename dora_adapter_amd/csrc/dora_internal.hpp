@@ -1,0 +1,94 @@
+// dora_internal.hpp - types shared by the HIP kernels and the C-ABI layer of
+// libdora.so (gfx950).  Not part of the public interface (include/dora.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dora {
+
+// ---------------------------------------------------------------- GEMM plan
+// C[M, N] = sum over segments of op(A_seg) * op(B_seg), accumulated in fp32.
+// A_seg is K-major ([M][lda], K contiguous) or MN-major ([K][lda], M
+// contiguous); likewise B_seg ([N][ldb] or [K][ldb]).  Up to two segments
+// are concatenated along K (e.g. dx = [dh | Q] [W ; A]).  Each segment's K
+// range is walked in BK-wide steps with the tail zero-filled, and split-K
+// slices the concatenated step list into `splits` contiguous ranges
+// (blockIdx.y).
+struct GemmSeg {
+    const void *a;
+    int64_t lda;
+    const void *b;
+    int64_t ldb;
+    int64_t K;
+};
+
+enum EpiMode : int {
+    EPI_STORE = 0,   // out[m, n] = alpha * C (dtype of the kernel or fp32), split z at out + z*M*ldc
+    EPI_ROWDOT = 1,  // rowdot[(z*ntn + tn)*M + m] = sum_{n in tile} C[m, n] * E[m, n]
+};
+
+struct GemmArgs {
+    int64_t M, N;
+    GemmSeg seg[2];
+    int nseg;
+    int splits;
+    int64_t steps_per_split;  // BK-steps per split slice
+    int mode;
+    // EPI_STORE
+    void *out;
+    int64_t ldc;
+    int out_f32;             // 1: fp32 output (split-K partials); 0: kernel dtype
+    float alpha;
+    // EPI_ROWDOT
+    const void *E;
+    int64_t lde;
+    float *rowdot;
+    // optional sum of squares of A's rows over each split's K range (K-major
+    // A only; written by the tiles of the first N block): rowsq[z*M + m]
+    float *rowsq;
+};
+
+// Launchers (gemm_bf16.hip / gemm_f32.hip).  `layout` selects the operand
+// orders: 0 = A K-major, B K-major (C = A B^T); 1 = A K-major, B MN-major
+// (C = A B); 2 = A MN-major, B MN-major (C = A^T B).  `cfg` picks the tile
+// shape (see gemm_configs in the .hip file).
+hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, hipStream_t st);
+hipError_t launch_gemm_f32(const GemmArgs &a, int layout, bool rowsq, hipStream_t st);
+
+// Tile shapes of the bf16 MFMA GEMM, indexable by `cfg`.
+struct TileCfg {
+    int BM, BN;
+    float rel_speed;  // relative MFMA efficiency of a full tile, for planning
+};
+int gemm_bf16_num_cfgs();
+TileCfg gemm_bf16_cfg(int cfg);
+constexpr int GEMM_BK = 64;      // bf16 K step
+constexpr int GEMM_F32_BM = 64;  // fp32 VALU tile
+constexpr int GEMM_F32_BN = 64;
+constexpr int GEMM_F32_BK = 16;
+
+// Elementwise / reduction kernels (elementwise.hip).  `bf16` selects the
+// matrix element type (1: bf16, 0: fp32).
+hipError_t launch_compose(int bf16, const void *base, const void *lora, const float *m,
+                          const float *n, float s, int64_t T, int64_t d_out, void *y,
+                          hipStream_t st);
+hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t M, int64_t N,
+                                float alpha, void *out, hipStream_t st);
+hipError_t launch_gram_finalize(int bf16, const float *part, int splits, int64_t r, void *G_out,
+                                hipStream_t st);
+hipError_t launch_norm_finish(const float *base_part, int zb, const float *cross_part, int zc,
+                              const float *gram_part, int zg, int64_t d_out, float s, float *n,
+                              float *base, float *cross, float *gram, hipStream_t st);
+hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const float *m,
+                                const float *n, int64_t T, int64_t d_out, int64_t t_chunk,
+                                void *dh, float *dm_part, hipStream_t st);
+hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, int64_t d_out,
+                            float *dm, hipStream_t st);
+hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st);
+hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
+
+// dh/dm partial sums: rows of T per chunk and number of chunks.
+int64_t dm_t_chunk(int64_t T, int64_t d_out);
+
+}  // namespace dora

@@ -1,0 +1,418 @@
+// elementwise.hip - the HBM-bound kernels of the DoRA module (gfx950).
+//
+//   compose      y = base + ((g - 1) base + g s lora), g = m / n: the single
+//                pass with the cancellation-safe near-unity form ("Scaling
+//                DoRA" abstract, fused compose).  6 bytes per bf16 element.
+//   dh / dm      dh = g dy and dm_i = sum_t dy y / m_i for the norm-detached
+//                backward (DoRA summary, "Statistical analysis"), one pass
+//                over dy and y with fixed-order partial sums.
+//   small ones   split-K reduction, Gram matrix finalisation (fp32 sum of
+//                split partials, bf16 hi/lo split), the row-norm finish.
+//
+// Streaming layout: a thread owns one group of 8 consecutive columns and a
+// contiguous run of rows, so per-column factors (g - 1, g s) are formed once
+// per run and every row access is a 16-byte load/store, consecutive threads
+// covering consecutive 16-byte groups of a row (fully coalesced).
+#include "dora_internal.hpp"
+#include "epilogue.hpp"
+
+namespace dora {
+namespace {
+
+constexpr int EW_THREADS = 256;
+// Threads a streaming launch aims for: 256 CUs x 8 wavefronts x 64 lanes x 4.
+constexpr int64_t EW_TARGET_THREADS = 256LL * 8 * 64 * 4;
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<uint16_t> {
+    __device__ static void load(const uint16_t *p, float (&v)[8])
+    {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(w[q] << 16);
+            v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        }
+    }
+    __device__ static void store(uint16_t *p, const float (&v)[8])
+    {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+    __device__ static float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+    __device__ static void store1(uint16_t *p, float v) { *p = f32_to_bf16(v); }
+};
+template <>
+struct Vec8<float> {
+    __device__ static void load(const float *p, float (&v)[8])
+    {
+        const float4 a = reinterpret_cast<const float4 *>(p)[0];
+        const float4 b = reinterpret_cast<const float4 *>(p)[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    __device__ static void store(float *p, const float (&v)[8])
+    {
+        reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __device__ static float load1(const float *p) { return *p; }
+    __device__ static void store1(float *p, float v) { *p = v; }
+};
+
+// Rows per thread run for a [T, d_out] stream with gpr column groups.
+__host__ __device__ inline int64_t rows_per_run(int64_t T, int64_t gpr)
+{
+    int64_t runs = EW_TARGET_THREADS / (gpr > 0 ? gpr : 1);
+    if (runs < 1)
+        runs = 1;
+    if (runs > T)
+        runs = T;
+    return runs > 0 ? (T + runs - 1) / runs : 1;
+}
+
+// One compose element in the stable form: y = b + ((g - 1) b + g s l).
+__device__ __forceinline__ float compose1(float b, float l, float gm1, float gs)
+{
+    return b + __fmaf_rn(gm1, b, gs * l);
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(EW_THREADS)
+    compose_kernel(const T *__restrict__ base, const T *__restrict__ lora,
+                   const float *__restrict__ m, const float *__restrict__ n, float s, int64_t Tn,
+                   int64_t d_out, int64_t rows, T *y)
+{
+    const int64_t gpr = (d_out + 7) / 8;
+    const int64_t gi = static_cast<int64_t>(blockIdx.x) * EW_THREADS + threadIdx.x;
+    const int64_t c = gi % gpr, run = gi / gpr;
+    const int64_t t0 = run * rows;
+    if (t0 >= Tn)
+        return;
+    const int64_t t1 = (t0 + rows) < Tn ? (t0 + rows) : Tn;
+    const int64_t i0 = c * 8;
+    const int cnt = (d_out - i0) < 8 ? static_cast<int>(d_out - i0) : 8;
+    float gm1[8], gs[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float mi = q < cnt ? m[i0 + q] : 1.f;
+        const float ni = q < cnt ? n[i0 + q] : 1.f;
+        gm1[q] = (mi - ni) / ni;  // exact m - n when n/2 <= m <= 2n (Sterbenz)
+        gs[q] = (mi / ni) * s;
+    }
+    if (VEC) {
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t off = t * d_out + i0;
+            float b[8], l[8], o[8];
+            Vec8<T>::load(base + off, b);
+            Vec8<T>::load(lora + off, l);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                o[q] = compose1(b[q], l[q], gm1[q], gs[q]);
+            Vec8<T>::store(y + off, o);
+        }
+    } else {
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t off = t * d_out + i0;
+            for (int q = 0; q < cnt; ++q)
+                Vec8<T>::store1(y + off + q, compose1(Vec8<T>::load1(base + off + q),
+                                                      Vec8<T>::load1(lora + off + q), gm1[q],
+                                                      gs[q]));
+        }
+    }
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(EW_THREADS)
+    dh_dm_kernel(const T *__restrict__ dy, const T *__restrict__ yv, const float *__restrict__ m,
+                 const float *__restrict__ n, int64_t Tn, int64_t d_out, int64_t rows,
+                 T *__restrict__ dh, float *__restrict__ dm_part)
+{
+    const int64_t gpr = (d_out + 7) / 8;
+    const int64_t gi = static_cast<int64_t>(blockIdx.x) * EW_THREADS + threadIdx.x;
+    const int64_t c = gi % gpr, run = gi / gpr;
+    const int64_t t0 = run * rows;
+    if (t0 >= Tn)
+        return;
+    const int64_t t1 = (t0 + rows) < Tn ? (t0 + rows) : Tn;
+    const int64_t i0 = c * 8;
+    const int cnt = (d_out - i0) < 8 ? static_cast<int>(d_out - i0) : 8;
+    float g[8], acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        g[q] = q < cnt ? m[i0 + q] / n[i0 + q] : 0.f;
+        acc[q] = 0.f;
+    }
+    if (VEC) {
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t off = t * d_out + i0;
+            float a[8], b[8], o[8];
+            Vec8<T>::load(dy + off, a);
+            Vec8<T>::load(yv + off, b);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                o[q] = g[q] * a[q];
+                acc[q] = __fmaf_rn(a[q], b[q], acc[q]);
+            }
+            Vec8<T>::store(dh + off, o);
+        }
+    } else {
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t off = t * d_out + i0;
+            for (int q = 0; q < cnt; ++q) {
+                const float a = Vec8<T>::load1(dy + off + q);
+                Vec8<T>::store1(dh + off + q, g[q] * a);
+                acc[q] = __fmaf_rn(a, Vec8<T>::load1(yv + off + q), acc[q]);
+            }
+        }
+    }
+    for (int q = 0; q < cnt; ++q)
+        dm_part[run * d_out + i0 + q] = acc[q];
+}
+
+__global__ void dm_finish_kernel(const float *__restrict__ part, int nchunks,
+                                 const float *__restrict__ m, int64_t d_out, float *__restrict__ dm)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= d_out)
+        return;
+    float acc = 0.f;
+    for (int k = 0; k < nchunks; ++k)
+        acc += part[static_cast<int64_t>(k) * d_out + i];
+    dm[i] = acc / m[i];
+}
+
+template <typename T>
+__global__ void splitk_reduce_kernel(const float *__restrict__ part, int splits, int64_t MN,
+                                     float alpha, T *__restrict__ out)
+{
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < MN;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float acc = 0.f;
+        for (int z = 0; z < splits; ++z)
+            acc += part[static_cast<int64_t>(z) * MN + e];
+        Vec8<T>::store1(out + e, alpha * acc);
+    }
+}
+
+// G = sum_z part[z] (fixed order).  bf16: writes G_hi = bf16(G) into rows
+// [0, r) and G_lo = bf16(G - G_hi) into rows [r, 2r) of a [2r, r] matrix, so
+// that B G = B G_hi + B G_lo keeps about 16 bits of G on bf16 MFMAs.
+// fp32: writes G itself.
+__global__ void gram_finalize_kernel(const float *__restrict__ part, int splits, int64_t r, int bf16,
+                                     void *__restrict__ G_out)
+{
+    const int64_t rr = r * r;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < rr;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float acc = 0.f;
+        for (int z = 0; z < splits; ++z)
+            acc += part[static_cast<int64_t>(z) * rr + e];
+        if (bf16) {
+            uint16_t *G = static_cast<uint16_t *>(G_out);
+            const uint16_t hi = f32_to_bf16(acc);
+            G[e] = hi;
+            G[rr + e] = f32_to_bf16(acc - bf16_to_f32(hi));
+        } else {
+            static_cast<float *>(G_out)[e] = acc;
+        }
+    }
+}
+
+// n_i = sqrt(max(base + 2 s cross + s^2 gram, 0)) from fixed-order sums of
+// the per-split / per-tile partials, combined in fp64.
+__global__ void norm_finish_kernel(const float *__restrict__ bp, int zb, const float *__restrict__ cp,
+                                   int zc, const float *__restrict__ gp, int zg, int64_t d_out,
+                                   float s, float *__restrict__ n, float *base, float *cross,
+                                   float *gram)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= d_out)
+        return;
+    double b = 0.0, c = 0.0, g = 0.0;
+    for (int z = 0; z < zb; ++z)
+        b += bp[static_cast<int64_t>(z) * d_out + i];
+    for (int z = 0; z < zc; ++z)
+        c += cp[static_cast<int64_t>(z) * d_out + i];
+    for (int z = 0; z < zg; ++z)
+        g += gp[static_cast<int64_t>(z) * d_out + i];
+    const double sd = static_cast<double>(s);
+    double n2 = b + 2.0 * sd * c + sd * sd * g;
+    if (n2 < 0.0)
+        n2 = 0.0;
+    n[i] = static_cast<float>(sqrt(n2));
+    if (base)
+        base[i] = static_cast<float>(b);
+    if (cross)
+        cross[i] = static_cast<float>(c);
+    if (gram)
+        gram[i] = static_cast<float>(g);
+}
+
+__global__ void copy_f32_kernel(const float *__restrict__ src, float *__restrict__ dst, int64_t n)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n)
+        dst[i] = src[i];
+}
+
+__global__ void fill_f32_kernel(float *__restrict__ dst, float v, int64_t n)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n)
+        dst[i] = v;
+}
+
+unsigned blocks_for(int64_t threads)
+{
+    return static_cast<unsigned>((threads + EW_THREADS - 1) / EW_THREADS);
+}
+
+}  // namespace
+
+int64_t dm_t_chunk(int64_t T, int64_t d_out)
+{
+    return rows_per_run(T, (d_out + 7) / 8);
+}
+
+hipError_t launch_compose(int bf16, const void *base, const void *lora, const float *m,
+                          const float *n, float s, int64_t T, int64_t d_out, void *y,
+                          hipStream_t st)
+{
+    if (T == 0 || d_out == 0)
+        return hipSuccess;
+    const int64_t gpr = (d_out + 7) / 8;
+    const int64_t rows = rows_per_run(T, gpr);
+    const int64_t runs = (T + rows - 1) / rows;
+    const dim3 grid(blocks_for(gpr * runs));
+    const bool vec = (d_out % 8) == 0;
+    if (bf16) {
+        auto *b = static_cast<const uint16_t *>(base);
+        auto *l = static_cast<const uint16_t *>(lora);
+        auto *o = static_cast<uint16_t *>(y);
+        if (vec)
+            hipLaunchKernelGGL((compose_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0, st, b, l,
+                               m, n, s, T, d_out, rows, o);
+        else
+            hipLaunchKernelGGL((compose_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0, st, b,
+                               l, m, n, s, T, d_out, rows, o);
+    } else {
+        auto *b = static_cast<const float *>(base);
+        auto *l = static_cast<const float *>(lora);
+        auto *o = static_cast<float *>(y);
+        if (vec)
+            hipLaunchKernelGGL((compose_kernel<float, true>), grid, dim3(EW_THREADS), 0, st, b, l, m,
+                               n, s, T, d_out, rows, o);
+        else
+            hipLaunchKernelGGL((compose_kernel<float, false>), grid, dim3(EW_THREADS), 0, st, b, l,
+                               m, n, s, T, d_out, rows, o);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const float *m,
+                                const float *n, int64_t T, int64_t d_out, int64_t t_chunk,
+                                void *dh, float *dm_part, hipStream_t st)
+{
+    if (T == 0 || d_out == 0)
+        return hipSuccess;
+    const int64_t gpr = (d_out + 7) / 8;
+    const int64_t runs = (T + t_chunk - 1) / t_chunk;
+    const dim3 grid(blocks_for(gpr * runs));
+    const bool vec = (d_out % 8) == 0;
+    if (bf16) {
+        auto *a = static_cast<const uint16_t *>(dy);
+        auto *b = static_cast<const uint16_t *>(y);
+        auto *o = static_cast<uint16_t *>(dh);
+        if (vec)
+            hipLaunchKernelGGL((dh_dm_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0, st, a, b,
+                               m, n, T, d_out, t_chunk, o, dm_part);
+        else
+            hipLaunchKernelGGL((dh_dm_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0, st, a, b,
+                               m, n, T, d_out, t_chunk, o, dm_part);
+    } else {
+        auto *a = static_cast<const float *>(dy);
+        auto *b = static_cast<const float *>(y);
+        auto *o = static_cast<float *>(dh);
+        if (vec)
+            hipLaunchKernelGGL((dh_dm_kernel<float, true>), grid, dim3(EW_THREADS), 0, st, a, b, m,
+                               n, T, d_out, t_chunk, o, dm_part);
+        else
+            hipLaunchKernelGGL((dh_dm_kernel<float, false>), grid, dim3(EW_THREADS), 0, st, a, b, m,
+                               n, T, d_out, t_chunk, o, dm_part);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, int64_t d_out,
+                            float *dm, hipStream_t st)
+{
+    if (d_out == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(dm_finish_kernel, dim3(blocks_for(d_out)), dim3(EW_THREADS), 0, st, dm_part,
+                       nchunks, m, d_out, dm);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t M, int64_t N,
+                                float alpha, void *out, hipStream_t st)
+{
+    const int64_t MN = M * N;
+    if (MN == 0)
+        return hipSuccess;
+    int64_t blocks = (MN + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 8192)
+        blocks = 8192;
+    if (bf16)
+        hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(EW_THREADS), 0, st, part, splits, MN, alpha,
+                           static_cast<uint16_t *>(out));
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(EW_THREADS), 0, st, part, splits, MN, alpha,
+                           static_cast<float *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_gram_finalize(int bf16, const float *part, int splits, int64_t r, void *G_out,
+                                hipStream_t st)
+{
+    int64_t blocks = (r * r + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 4096)
+        blocks = 4096;
+    hipLaunchKernelGGL(gram_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(EW_THREADS), 0,
+                       st, part, splits, r, bf16, G_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_finish(const float *base_part, int zb, const float *cross_part, int zc,
+                              const float *gram_part, int zg, int64_t d_out, float s, float *n,
+                              float *base, float *cross, float *gram, hipStream_t st)
+{
+    if (d_out == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(norm_finish_kernel, dim3(blocks_for(d_out)), dim3(EW_THREADS), 0, st,
+                       base_part, zb, cross_part, zc, gram_part, zg, d_out, s, n, base, cross, gram);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(n)), dim3(EW_THREADS), 0, st, src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(n)), dim3(EW_THREADS), 0, st, dst, v, n);
+    return hipGetLastError();
+}
+
+}  // namespace dora

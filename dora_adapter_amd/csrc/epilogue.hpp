@@ -1,0 +1,142 @@
+// epilogue.hpp - GEMM epilogues shared by the bf16 MFMA and fp32 VALU GEMMs.
+//
+// After the K loop a workgroup stages R rows of its fp32 accumulator tile in
+// LDS (Cs, row stride CST floats) and calls epilogue_rows, which either
+// stores alpha*C (rounded once to bf16, or fp32) with 16-byte coalesced
+// writes, or reduces each row of C (.) E to one partial dot product.  The
+// row-dot mode is how the factored norm's cross term (rows of B against
+// U = W A^T) and Gram term (rows of B against B G) are formed without U or
+// B G ever reaching HBM.
+#pragma once
+
+#include "dora_internal.hpp"
+
+namespace dora {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h)
+{
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename TE>
+__device__ __forceinline__ float load_elem(const TE *p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p, int64_t i)
+{
+    return bf16_to_f32(p[i]);
+}
+template <>
+__device__ __forceinline__ float load_elem<float>(const float *p, int64_t i)
+{
+    return p[i];
+}
+
+// Process rows [mrow0, mrow0 + R) of the tile whose first column is n0.
+// Every thread of the workgroup must call this (row-dot uses wave shuffles).
+template <int R, int BN, int CST, int NT, typename TE>
+__device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g, int64_t mrow0,
+                                              int64_t n0, int z, int tn, int tid)
+{
+    constexpr int CPR = BN / 8;  // 8-column chunks per row
+    static_assert(BN % 8 == 0 && 64 % CPR == 0, "row chunks must tile a wavefront");
+    static_assert((R * CPR) % NT == 0, "every thread takes the same number of chunks");
+    const int64_t M = g.M, N = g.N;
+
+    if (g.mode == EPI_STORE) {
+        for (int idx = tid; idx < R * CPR; idx += NT) {
+            const int row = idx / CPR, c = idx % CPR;
+            const int64_t m = mrow0 + row, n = n0 + c * 8;
+            if (m >= M || n >= N)
+                continue;
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] = g.alpha * Cs[row * CST + c * 8 + q];
+            const int cnt = (N - n) < 8 ? static_cast<int>(N - n) : 8;
+            if (g.out_f32) {
+                float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * M * g.ldc +
+                           m * g.ldc + n;
+                if (cnt == 8 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
+                    reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+                    reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+                } else {
+                    for (int q = 0; q < cnt; ++q)
+                        o[q] = v[q];
+                }
+            } else if constexpr (sizeof(TE) == 2) {
+                uint16_t *o = static_cast<uint16_t *>(g.out) + m * g.ldc + n;
+                if (cnt == 8) {
+                    *reinterpret_cast<uint4 *>(o) =
+                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+                } else {
+                    for (int q = 0; q < cnt; ++q)
+                        o[q] = f32_to_bf16(v[q]);
+                }
+            } else {
+                float *o = static_cast<float *>(g.out) + m * g.ldc + n;
+                for (int q = 0; q < cnt; ++q)
+                    o[q] = v[q];
+            }
+        }
+    } else {  // EPI_ROWDOT
+        const int ntn = static_cast<int>((N + BN - 1) / BN);
+        const TE *E = static_cast<const TE *>(g.E);
+        for (int idx = tid; idx < R * CPR; idx += NT) {
+            const int row = idx / CPR, c = idx % CPR;
+            const int64_t m = mrow0 + row, n = n0 + c * 8;
+            float sum = 0.f;
+            if (m < M && n < N) {
+                const int cnt = (N - n) < 8 ? static_cast<int>(N - n) : 8;
+                for (int q = 0; q < cnt; ++q)
+                    sum += Cs[row * CST + c * 8 + q] * load_elem<TE>(E, m * g.lde + n + q);
+            }
+#pragma unroll
+            for (int off = CPR / 2; off >= 1; off >>= 1)
+                sum += __shfl_xor(sum, off);
+            if (c == 0 && m < M)
+                g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * M + m] = sum;
+        }
+    }
+}
+
+// Map the linear workgroup id to a (tile row, tile column).  Consecutive
+// hardware workgroup ids go to the 8 XCDs in turn; each XCD is given a
+// contiguous run of logical tiles, and logical tiles are ordered in groups
+// of 8 tile rows so that the workgroups resident on one XCD at a time share
+// A rows and B columns in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN, int &tm, int &tn)
+{
+    const int nb = static_cast<int>(gridDim.x);
+    const int b = static_cast<int>(blockIdx.x);
+    const int q = nb >> 3, rem = nb & 7;
+    const int xcd = b & 7, local = b >> 3;
+    const int L = (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+    const int num_m = static_cast<int>((M + BM - 1) / BM);
+    const int num_n = static_cast<int>((N + BN - 1) / BN);
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * num_n;
+    const int group = L / per_group;
+    const int first_m = group * GROUP;
+    const int gsz = (num_m - first_m) < GROUP ? (num_m - first_m) : GROUP;
+    const int in_g = L - group * per_group;
+    tm = first_m + in_g % gsz;
+    tn = in_g / gsz;
+}
+
+}  // namespace dora

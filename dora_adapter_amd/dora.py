@@ -1,0 +1,200 @@
+"""Thin ctypes binding of libdora.so (include/dora.h), same names as the C ABI.
+
+Argument marshalling only: tensors are passed as device pointers, outputs and
+the workspace are allocated with torch (device memory plumbing), and every
+step of the computation runs in the library's HIP kernels.  There is no CPU
+or PyTorch fallback: if the library is missing or cannot be loaded, every
+call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdora.so")
+
+DORA_F32, DORA_BF16 = 0, 1
+STATUS = {0: "DORA_OK", 1: "DORA_E_NULL", 2: "DORA_E_SHAPE", 3: "DORA_E_DTYPE",
+          4: "DORA_E_ALIGN", 5: "DORA_E_WORKSPACE", 6: "DORA_E_ALIAS", 7: "DORA_E_HIP"}
+
+# Every symbol include/dora.h declares.
+EXPORTS = ("dora_strerror", "dora_last_error", "dora_norm_workspace", "dora_forward_workspace",
+           "dora_backward_workspace", "dora_factored_norm", "dora_compose", "dora_forward",
+           "dora_backward", "dora_linear_workspace", "dora_linear")
+
+_lib = None
+
+
+class DoraError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libdora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, sz, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        c_int = ctypes.c_int
+        L.dora_strerror.restype = ctypes.c_char_p
+        L.dora_strerror.argtypes = [c_int]
+        L.dora_last_error.restype = ctypes.c_char_p
+        L.dora_last_error.argtypes = []
+        L.dora_norm_workspace.restype = sz
+        L.dora_norm_workspace.argtypes = [i64, i64, i64, c_int]
+        L.dora_forward_workspace.restype = sz
+        L.dora_forward_workspace.argtypes = [i64, i64, i64, i64, c_int]
+        L.dora_backward_workspace.restype = sz
+        L.dora_backward_workspace.argtypes = [i64, i64, i64, i64, c_int]
+        L.dora_factored_norm.restype = c_int
+        L.dora_factored_norm.argtypes = [p, p, p, f, i64, i64, i64, c_int, p, p, p, p, p, sz, p]
+        L.dora_compose.restype = c_int
+        L.dora_compose.argtypes = [p, p, p, p, f, i64, i64, c_int, p, p]
+        L.dora_forward.restype = c_int
+        L.dora_forward.argtypes = [p, p, p, p, p, f, i64, i64, i64, i64, c_int, p, p, p, p, p,
+                                   sz, p]
+        L.dora_backward.restype = c_int
+        L.dora_backward.argtypes = [p, p, p, p, p, p, p, f, p, p, i64, i64, i64, i64, c_int, p,
+                                    p, p, p, p, sz, p]
+        L.dora_linear_workspace.restype = sz
+        L.dora_linear_workspace.argtypes = [i64, i64, i64, c_int]
+        L.dora_linear.restype = c_int
+        L.dora_linear.argtypes = [p, p, i64, i64, i64, c_int, p, p, sz, p]
+        _lib = L
+    return _lib
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return DORA_BF16
+    if t.dtype == torch.float32:
+        return DORA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(rc):
+    if rc != 0:
+        raise DoraError(rc, lib().dora_last_error().decode())
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("libdora needs device tensors")
+    return t.device
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def dora_norm_workspace(d_out, d_in, r, dtype):
+    return lib().dora_norm_workspace(d_out, d_in, r, dtype)
+
+
+def dora_forward_workspace(T, d_in, d_out, r, dtype):
+    return lib().dora_forward_workspace(T, d_in, d_out, r, dtype)
+
+
+def dora_backward_workspace(T, d_in, d_out, r, dtype):
+    return lib().dora_backward_workspace(T, d_in, d_out, r, dtype)
+
+
+def dora_factored_norm(W, A, B, s, terms=False, ws=None, n=None):
+    """Row norms of W + s*B*A (fp32 [d_out]); with terms=True also returns
+    (base, cross, gram)."""
+    dev = _dev(W)
+    d_out, d_in = W.shape
+    r = A.shape[0]
+    dt = _dt(W)
+    n = torch.empty(d_out, dtype=torch.float32, device=dev) if n is None else n
+    extra = [torch.empty(d_out, dtype=torch.float32, device=dev) for _ in range(3)] if terms \
+        else [None, None, None]
+    need = lib().dora_norm_workspace(d_out, d_in, r, dt)
+    ws = _ws(need, dev) if ws is None else ws
+    _check(lib().dora_factored_norm(_ptr(W), _ptr(A), _ptr(B), float(s), d_out, d_in, r, dt,
+                                    _ptr(n), *[_ptr(e) for e in extra], _ptr(ws),
+                                    ws.numel(), _stream(dev)))
+    return (n, *extra) if terms else n
+
+
+def dora_compose(base, lora, m, n, s, y=None):
+    """y = (m/n) (.) (base + s*lora) in the stable single-pass form; y may be base."""
+    dev = _dev(base)
+    T, d_out = base.shape
+    y = torch.empty_like(base) if y is None else y
+    _check(lib().dora_compose(_ptr(base), _ptr(lora), _ptr(m), _ptr(n), float(s), T, d_out,
+                              _dt(base), _ptr(y), _stream(dev)))
+    return y
+
+
+def dora_forward(x, W, A, B, m, s, n_in=None, want_P=True, ws=None, y=None, n_out=None,
+                 P_out=None):
+    """Module forward.  Returns (y, n, P) (P is None when want_P is False)."""
+    dev = _dev(x)
+    T, d_in = x.shape
+    d_out = W.shape[0]
+    r = A.shape[0]
+    dt = _dt(x)
+    y = torch.empty(T, d_out, dtype=x.dtype, device=dev) if y is None else y
+    n_out = torch.empty(d_out, dtype=torch.float32, device=dev) if n_out is None else n_out
+    if want_P and P_out is None:
+        P_out = torch.empty(T, r, dtype=x.dtype, device=dev)
+    need = lib().dora_forward_workspace(T, d_in, d_out, r, dt)
+    ws = _ws(need, dev) if ws is None else ws
+    _check(lib().dora_forward(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), float(s), T, d_in,
+                              d_out, r, dt, _ptr(y), _ptr(n_out), _ptr(P_out if want_P else None),
+                              _ptr(n_in), _ptr(ws), ws.numel(), _stream(dev)))
+    return y, n_out, (P_out if want_P else None)
+
+
+def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None):
+    """Norm-detached backward.  Returns dict(dx, dA, dB, dm)."""
+    dev = _dev(W)
+    T, d_in = x.shape
+    d_out = W.shape[0]
+    r = A.shape[0]
+    dt = _dt(W)
+    if out is None:
+        out = {"dx": torch.empty(T, d_in, dtype=W.dtype, device=dev),
+               "dA": torch.empty(r, d_in, dtype=W.dtype, device=dev),
+               "dB": torch.empty(d_out, r, dtype=W.dtype, device=dev),
+               "dm": torch.empty(d_out, dtype=torch.float32, device=dev)}
+    need = lib().dora_backward_workspace(T, d_in, d_out, r, dt)
+    ws = _ws(need, dev) if ws is None else ws
+    _check(lib().dora_backward(_ptr(dy), _ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), _ptr(n),
+                               float(s), _ptr(P), _ptr(y), T, d_in, d_out, r, dt, _ptr(out["dx"]),
+                               _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dm"]), _ptr(ws),
+                               ws.numel(), _stream(dev)))
+    return out
+
+
+def dora_linear_workspace(T, d_in, d_out, dtype):
+    return lib().dora_linear_workspace(T, d_in, d_out, dtype)
+
+
+def dora_linear(x, W, y=None, ws=None):
+    """y = x W^T on the forward's base-product kernel (merged-weight inference)."""
+    dev = _dev(x)
+    T, d_in = x.shape
+    d_out = W.shape[0]
+    dt = _dt(x)
+    y = torch.empty(T, d_out, dtype=x.dtype, device=dev) if y is None else y
+    need = lib().dora_linear_workspace(T, d_in, d_out, dt)
+    if ws is None and need > 0:
+        ws = _ws(need, dev)
+    _check(lib().dora_linear(_ptr(x), _ptr(W), T, d_in, d_out, dt, _ptr(y), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(dev)))
+    return y

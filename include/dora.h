@@ -1,0 +1,190 @@
+/*
+ * dora.h - C ABI of libdora.so, the MI355X (gfx950) DoRA module hot path.
+ *
+ * Sources (by page title and section):
+ *   [SD]   "Scaling DoRA: High-Rank Adaptation via Factored Norms and Fused
+ *          Kernels" (Zelenin, Zhuravlyova; arXiv 2603.22276), abstract:
+ *          the row-wise norm of W + sBA, its factored form (base, cross and
+ *          Gram terms through O(d_out r + r^2) intermediates, no dense BA),
+ *          and the single-pass, cancellation-safe composition.
+ *   [DoRA] "DoRA: Weight-Decomposed Low-Rank Adaptation" (Liu et al. 2024),
+ *          summary pages: "Method" (magnitude m and a direction updated by
+ *          LoRA) and "Statistical analysis" (a training-memory modification,
+ *          read here as a norm held constant in the backward pass).
+ *
+ * Notation.  W [d_out, d_in] is the frozen weight, A [r, d_in] and
+ * B [d_out, r] the LoRA factors, s the LoRA scale, m [d_out] the magnitude,
+ * x [T, d_in] the tokens.  V = W + s*B*A is never formed.
+ *   n_i  = ||W_i + s*B_i*A||_2                       (row norm, [SD])
+ *   g_i  = m_i / n_i
+ *   y    = g (.) (x W^T + s * (x A^T) B^T)           ([SD], [DoRA])
+ *
+ * Conventions shared by every call:
+ *   - Every matrix is dense, row-major and contiguous.  Matrix data (x, W,
+ *     A, B, dy, y, P, base, lora, dx, dA, dB) has one element type given by
+ *     the dora_dtype argument.  m, n, dm and the optional norm terms are
+ *     always fp32.  s is an fp32 scalar passed by value.
+ *   - Every pointer is device memory owned by the caller (e.g. torch
+ *     tensors).  The library never allocates device memory and keeps no
+ *     state between calls; its only scratch is the caller's workspace
+ *     `ws` of at least the size the matching *_workspace() query returns.
+ *     No workspace size has a d_out*d_in term: no dense [d_out, d_in]
+ *     buffer is ever formed.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Arguments are
+ *     validated on the host before anything is enqueued; kernels then run
+ *     asynchronously on `stream` and results are valid once it is
+ *     synchronised.  Nothing inside synchronises the host.
+ *   - Every pointer must be 16-byte aligned.  For DORA_BF16, d_in, d_out
+ *     and r must be multiples of 8 (rows of 16 bytes); T may be any value
+ *     >= 0.  For DORA_F32 there is no multiple-of-8 requirement.  r >= 1
+ *     and d_in >= 1 always.
+ *   - Results are bitwise deterministic for identical inputs: there are no
+ *     floating-point atomics and every reduction runs in a fixed order.
+ *   - Arithmetic: products accumulate in fp32; matrix outputs are rounded
+ *     once, to nearest even, to the element type.
+ *   - Preconditions not checked per element: n_i > 0 (rows of W + sBA are
+ *     not zero) and, for dora_backward, m_i != 0.  Violations propagate
+ *     IEEE inf/NaN; they never fault.
+ *
+ * Errors: every call returns a dora_status.  On failure nothing has been
+ * enqueued unless the status is DORA_E_HIP (a launch failed part-way; the
+ * outputs are then unspecified).  dora_last_error() returns a thread-local
+ * message describing the last failure on the calling thread.
+ */
+#ifndef DORA_H
+#define DORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DORA_OK = 0,
+    DORA_E_NULL = 1,      /* a required pointer is NULL                      */
+    DORA_E_SHAPE = 2,     /* a size is out of range or breaks a multiple-of-8 rule */
+    DORA_E_DTYPE = 3,     /* unknown dora_dtype                              */
+    DORA_E_ALIGN = 4,     /* a pointer is not 16-byte aligned                */
+    DORA_E_WORKSPACE = 5, /* ws is NULL or ws_bytes is below the query       */
+    DORA_E_ALIAS = 6,     /* two buffers overlap where that is not allowed   */
+    DORA_E_HIP = 7        /* a HIP launch or runtime call failed             */
+} dora_status;
+
+typedef enum {
+    DORA_F32 = 0,  /* IEEE binary32 */
+    DORA_BF16 = 1  /* bfloat16 (upper 16 bits of binary32) */
+} dora_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char *dora_strerror(int status);
+
+/* Message for the last failure on the calling thread ("" if none). */
+const char *dora_last_error(void);
+
+/* Workspace sizes in bytes for the calls below (0 if the arguments are
+ * invalid).  They are pure host functions.  The norm workspace is
+ * O(d_out*r + r^2) for fixed splits, as [SD] states for the factored
+ * intermediates; forward and backward add O(T*d_out + T*r) activations. */
+size_t dora_norm_workspace(int64_t d_out, int64_t d_in, int64_t r, int dtype);
+size_t dora_forward_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype);
+size_t dora_backward_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype);
+
+/*
+ * dora_factored_norm - row norms of W + s*B*A without forming B*A ([SD]
+ * abstract, "factored norm"):
+ *     n_i^2 = base_i + 2*s*cross_i + s^2*gram_i
+ *     base_i  = sum_j W_ij^2
+ *     cross_i = sum_k B_ik * U_ik,        U = W A^T      [d_out, r]
+ *     gram_i  = sum_k B_ik * (B G)_ik,    G = A A^T      [r, r]
+ * n is written as sqrt(max(n^2, 0)) (the factored sum can round below
+ * zero only when ||W_i + s B_i A|| << ||W_i||).
+ *   W [d_out, d_in], A [r, d_in], B [d_out, r] in `dtype`.
+ *   n [d_out] fp32 (required).  base, cross, gram [d_out] fp32, each
+ *   optional (NULL to skip).
+ *   ws: device scratch of dora_norm_workspace(d_out, d_in, r, dtype) bytes.
+ */
+int dora_factored_norm(const void *W, const void *A, const void *B, float s,
+                       int64_t d_out, int64_t d_in, int64_t r, int dtype,
+                       float *n, float *base, float *cross, float *gram,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dora_compose - the single-pass composition ([SD] abstract, fused
+ * compose with a numerically stable form for the near-unity regime):
+ *     y[t,i] = base[t,i] + ( (g_i - 1) * base[t,i] + g_i * s * lora[t,i] )
+ * with g_i - 1 formed as (m_i - n_i) / n_i and g_i = m_i / n_i in fp32, the
+ * bracket summed before base is added, and one rounding to `dtype` at the
+ * end.  Mathematically y = (m/n) (.) (base + s*lora).
+ *   base, lora, y [T, d_out] in `dtype`; m, n [d_out] fp32.
+ *   y may be the same pointer as base (in place); any other overlap of y
+ *   with base or lora is DORA_E_ALIAS.
+ */
+int dora_compose(const void *base, const void *lora, const float *m, const float *n,
+                 float s, int64_t T, int64_t d_out, int dtype, void *y, void *stream);
+
+/*
+ * dora_forward - the DoRA module forward ([SD], [DoRA]):
+ *     n   = factored row norm (as dora_factored_norm), unless n_in is given
+ *     y   = x W^T                            (base, written into y)
+ *     P   = x A^T                            [T, r]
+ *     lra = P B^T                            [T, d_out], in the workspace
+ *     y   = compose(y, lra, m, n, s)         (as dora_compose, in place)
+ *   x [T, d_in], W [d_out, d_in], A [r, d_in], B [d_out, r] in `dtype`;
+ *   m [d_out] fp32.  y [T, d_out] in `dtype` (output).
+ *   n_out [d_out] fp32: receives n (required; with n_in it receives a copy).
+ *   P_out [T, r] in `dtype`: receives x A^T for the backward (NULL: kept in
+ *   the workspace only).
+ *   n_in [d_out] fp32 or NULL: a norm computed earlier (cached inference);
+ *   when given, the norm is not recomputed.
+ *   y must not overlap any input, n_out or P_out.
+ */
+int dora_forward(const void *x, const void *W, const void *A, const void *B, const float *m,
+                 float s, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype,
+                 void *y, float *n_out, void *P_out, const float *n_in,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dora_backward - gradients of L = sum(dy (.) y) with the row norm n held
+ * constant (stop-gradient; [DoRA] "Statistical analysis", training-memory
+ * modification).  With g = m / n and dh = g (.) dy:
+ *     dm_i = sum_t dy[t,i] * y[t,i] / m_i    (= sum_t dy h / n_i, h = x V^T)
+ *     Q    = s * dh B                        [T, r], in the workspace
+ *     dx   = dh W + Q A
+ *     dB   = s * dh^T P
+ *     dA   = Q^T x
+ * W is frozen and gets no gradient.  dx and dm equal the gradients without
+ * the stop-gradient (n does not depend on x or m); dA and dB omit the path
+ * through n.
+ *   dy, y [T, d_out], x [T, d_in], P [T, r] (from dora_forward), W, A, B in
+ *   `dtype`; m, n [d_out] fp32 (n as returned by dora_forward).
+ *   Outputs: dx [T, d_in], dA [r, d_in], dB [d_out, r] in `dtype`,
+ *   dm [d_out] fp32.  Outputs must not overlap each other or any input.
+ *   With T = 0, dA, dB and dm are zero.
+ */
+int dora_backward(const void *dy, const void *x, const void *W, const void *A, const void *B,
+                  const float *m, const float *n, float s, const void *P, const void *y,
+                  int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype,
+                  void *dx, void *dA, void *dB, float *dm,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dora_linear - y = x W^T on the same kernel and launch plan dora_forward
+ * uses for its base term.  With W = W' = g (.) (W + sBA), the weight merged
+ * after training, this is the whole DoRA inference path: the DoRA summary
+ * pages ("Method"; Key Points 3 and 5) note that the adapted weight merges
+ * into the base weight, adding no inference latency.
+ *   x [T, d_in], W [d_out, d_in], y [T, d_out] in `dtype`; y must not
+ *   overlap x or W.  ws: dora_linear_workspace(T, d_in, d_out, dtype) bytes
+ *   (0 when the product needs no split-K partials; ws may then be NULL).
+ */
+size_t dora_linear_workspace(int64_t T, int64_t d_in, int64_t d_out, int dtype);
+int dora_linear(const void *x, const void *W, int64_t T, int64_t d_in, int64_t d_out, int dtype,
+                void *y, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DORA_H */

@@ -1,0 +1,177 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol that
+include/dora.h declares, sizes its workspaces without any d_out*d_in term,
+and rejects bad arguments on the host before anything is enqueued.
+
+No call here reaches a kernel launch: every validation case breaks exactly
+one rule, and the pointers are fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dora_adapter_amd import dora as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dora.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_ALIAS = 0, 1, 2, 3, 4, 5, 6
+F32, BF16 = 0, 1
+FAKE = 1 << 40  # a 256-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dora_[a-z_]+)\s*\(", text)))
+
+
+def test_header_matches_binding_exports():
+    assert header_functions() == sorted(D.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = D.lib()
+    for name in header_functions():
+        assert hasattr(L, name), f"libdora.so does not export {name}"
+
+
+def test_strerror_and_last_error():
+    L = D.lib()
+    for code in range(8):
+        assert L.dora_strerror(code)
+    assert L.dora_strerror(99) == b"unknown status"
+    assert isinstance(L.dora_last_error(), bytes)
+
+
+def test_workspace_has_no_dense_term():
+    """No workspace grows with d_out*d_in.  The norm workspace is bounded by
+    O(r^2) split partials of G plus O(d_out) per-row partials, whatever d_in
+    is (a dense [d_out, d_in] bf16 buffer at d_in = 262144 would be 4 GiB);
+    the forward workspace grows with T*d_out (activations), not with d_in."""
+    L = D.lib()
+    r = 384
+    for d_out in (8192, 28672):
+        bound = 33 * r * r * 4 + 2 * r * r * 2 + 256 * d_out * 4
+        for d_in in (8192, 65536, 262144):
+            ws = L.dora_norm_workspace(d_out, d_in, r, BF16)
+            assert 0 < ws <= bound, (d_out, d_in, ws, bound)
+            assert ws < d_out * d_in * 2 / 8
+    f1 = L.dora_forward_workspace(2048, 8192, 8192, r, BF16)
+    f2 = L.dora_forward_workspace(2048, 65536, 8192, r, BF16)
+    f3 = L.dora_forward_workspace(4096, 8192, 8192, r, BF16)
+    # d_in x8 only moves split-K counts (capped at 32) of the O(T*r + r^2) partials
+    assert f2 - f1 <= 33 * (2048 * r + r * r) * 4
+    assert f3 - f1 >= 2048 * 8192 * 2              # T x2: one more lora [T, d_out] slab
+    assert L.dora_backward_workspace(2048, 8192, 8192, r, BF16) > 0
+
+
+def test_workspace_queries_reject_bad_shapes():
+    L = D.lib()
+    assert L.dora_norm_workspace(64, 100, 8, BF16) == 0      # d_in % 8
+    assert L.dora_norm_workspace(64, 128, 0, BF16) == 0      # r = 0
+    assert L.dora_forward_workspace(-1, 128, 64, 8, F32) == 0
+    assert L.dora_forward_workspace(16, 128, 64, 8, 7) == 0  # dtype
+    assert L.dora_norm_workspace(64, 100, 8, F32) > 0        # fp32: any width
+
+
+def test_library_source_never_allocates():
+    """The library's only scratch is the caller's workspace."""
+    csrc = os.path.join(ROOT, "dora_adapter_amd", "csrc")
+    for f in os.listdir(csrc):
+        text = open(os.path.join(csrc, f)).read()
+        for bad in ("hipMalloc", "hipFree", "malloc(", "new ", "hipHostMalloc"):
+            assert bad not in text, f"{f} calls {bad}"
+
+
+def _p(addr):
+    return ctypes.c_void_p(addr)
+
+
+def compose(base=FAKE, lora=FAKE + (1 << 30), m=FAKE + (2 << 30), n=FAKE + (3 << 30), s=1.0,
+            T=16, d_out=64, dt=BF16, y=FAKE + (4 << 30)):
+    return D.lib().dora_compose(_p(base), _p(lora), _p(m), _p(n), s, T, d_out, dt, _p(y), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"base": 0}, E_NULL), ({"y": 0}, E_NULL), ({"m": 0}, E_NULL),
+    ({"dt": 5}, E_DTYPE), ({"d_out": 60}, E_SHAPE), ({"T": -3}, E_SHAPE),
+    ({"lora": FAKE + 8}, E_ALIGN), ({"y": FAKE + 4}, E_ALIGN),
+    ({"y": FAKE + 16}, E_ALIAS),                      # partial overlap with base
+    ({"y": FAKE + (1 << 30) + 64}, E_ALIAS),         # overlaps lora
+])
+def test_compose_validation(kw, code):
+    assert compose(**kw) == code
+    assert D.lib().dora_last_error()
+
+
+def test_compose_fp32_any_width_passes_shape_check():
+    # fp32 accepts d_out = 60; break only the alignment so nothing launches.
+    assert compose(d_out=60, dt=F32, m=FAKE + (2 << 30) + 4) == E_ALIGN
+
+
+def _norm(W=FAKE, A=FAKE + (1 << 32), B=FAKE + (2 << 32), n=FAKE + (3 << 32), d_out=64,
+          d_in=128, r=8, dt=BF16, ws=FAKE + (4 << 32), ws_bytes=None, base=0):
+    L = D.lib()
+    if ws_bytes is None:
+        ws_bytes = max(L.dora_norm_workspace(d_out, d_in, r, BF16), 1)
+    return L.dora_factored_norm(_p(W), _p(A), _p(B), 1.0, d_out, d_in, r, dt, _p(n), _p(base),
+                                None, None, _p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"W": 0}, E_NULL), ({"n": 0}, E_NULL), ({"dt": 2}, E_DTYPE), ({"r": 0}, E_SHAPE),
+    ({"d_in": 100}, E_SHAPE), ({"d_out": 0}, E_SHAPE), ({"B": FAKE + (2 << 32) + 2}, E_ALIGN),
+    ({"ws": 0}, E_WS), ({"ws_bytes": 16}, E_WS),
+    ({"base": FAKE + (3 << 32) + 128}, E_ALIAS),       # base overlaps n
+    ({"n": FAKE + 256}, E_ALIAS),                      # n inside W
+])
+def test_norm_validation(kw, code):
+    assert _norm(**kw) == code
+
+
+def _fwd(x=FAKE, W=FAKE + (1 << 32), A=FAKE + (2 << 32), B=FAKE + (3 << 32),
+         m=FAKE + (4 << 32), T=16, d_in=128, d_out=64, r=8, dt=BF16, y=FAKE + (5 << 32),
+         n_out=FAKE + (6 << 32), P=0, n_in=0, ws=FAKE + (7 << 32), ws_bytes=None):
+    L = D.lib()
+    if ws_bytes is None:
+        ws_bytes = max(L.dora_forward_workspace(T, d_in, d_out, r, BF16), 1)
+    return L.dora_forward(_p(x), _p(W), _p(A), _p(B), _p(m), 1.0, T, d_in, d_out, r, dt, _p(y),
+                          _p(n_out), _p(P), _p(n_in), _p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"x": 0}, E_NULL), ({"n_out": 0}, E_NULL), ({"dt": -1}, E_DTYPE), ({"r": 12}, E_SHAPE),
+    ({"m": FAKE + (4 << 32) + 4}, E_ALIGN), ({"ws_bytes": 1}, E_WS),
+    ({"y": FAKE + 1024}, E_ALIAS),                     # y inside x
+    ({"P": FAKE + (5 << 32) + 512}, E_ALIAS),          # P_out inside y
+    ({"ws": FAKE + (2 << 32)}, E_ALIAS),               # workspace over A
+])
+def test_forward_validation(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_backward_validation():
+    L = D.lib()
+    T, d_in, d_out, r = 16, 128, 64, 8
+    need = L.dora_backward_workspace(T, d_in, d_out, r, BF16)
+    base = [FAKE + (k << 32) for k in range(16)]
+
+    def call(**kw):
+        a = dict(dy=base[0], x=base[1], W=base[2], A=base[3], B=base[4], m=base[5], n=base[6],
+                 P=base[7], y=base[8], dx=base[9], dA=base[10], dB=base[11], dm=base[12],
+                 ws=base[13], ws_bytes=need, T=T)
+        a.update(kw)
+        return L.dora_backward(_p(a["dy"]), _p(a["x"]), _p(a["W"]), _p(a["A"]), _p(a["B"]),
+                               _p(a["m"]), _p(a["n"]), 1.0, _p(a["P"]), _p(a["y"]), a["T"], d_in,
+                               d_out, r, BF16, _p(a["dx"]), _p(a["dA"]), _p(a["dB"]), _p(a["dm"]),
+                               _p(a["ws"]), a["ws_bytes"], None)
+
+    assert call(dy=0) == E_NULL
+    assert call(dm=0) == E_NULL
+    assert call(dA=base[10] + 2) == E_ALIGN
+    assert call(ws_bytes=need - 1) == E_WS
+    assert call(dx=base[0]) == E_ALIAS                  # dx over dy
+    assert call(dB=base[10] + 64) == E_ALIAS            # dB inside dA
+    assert call(T=-1) == E_SHAPE

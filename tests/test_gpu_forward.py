@@ -1,0 +1,146 @@
+"""GPU parity: dora_forward vs the oracle's dense y = (m/n)(x (W + sBA)^T).
+
+Full comparisons at sizes the oracle finishes in seconds (several tiles,
+ragged token counts), the tiny fp32 module, the invariants (B = 0 with
+m = n returns the base product; m = n returns plain LoRA; a cached norm
+reproduces the recomputed one bit for bit), and the full module shapes on
+sampled (token, row) entries."""
+import numpy as np
+import pytest
+import torch
+
+from dora_adapter_amd import dora as D
+from dora_adapter_amd import synth
+from gpu_util import check_close, check_norm, gpu, np64, say, sample_ids
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(mod, **kw):
+    t = {k: gpu(mod[k]) for k in ("x", "W", "A", "B", "m")}
+    y, n, P = D.dora_forward(t["x"], t["W"], t["A"], t["B"], t["m"], mod["s"], **kw)
+    torch.cuda.synchronize()
+    return y, n, P, t
+
+
+def test_tiny_fp32_module():
+    say("forward tiny fp32")
+    mod = synth.make_module(synth.TINY_F32, seed=0)
+    y, n, P, _ = _run(mod)
+    ref_y, ref_n = O.forward(mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], mod["s"])
+    check_norm(n, ref_n, torch.float32)
+    check_close(y, ref_y, torch.float32, "y tiny fp32")
+    P_ref = np64(mod["x"]) @ np64(mod["A"]).T
+    check_close(P, P_ref, torch.float32, "P tiny fp32")
+
+
+@pytest.mark.parametrize("T,d_out,d_in,r,s", [
+    (300, 264, 520, 24, 1.0),
+    (777, 1000, 1024, 40, 2.0),
+    (1, 512, 384, 384, 1.0),
+    (513, 384, 2048, 128, 0.5),
+])
+def test_bf16_matches_oracle(T, d_out, d_in, r, s):
+    say("forward bf16", T, d_out, d_in, r)
+    mod = synth.custom(d_out, d_in, r, T, "bf16", s, sigma_B=0.02, seed=T)
+    y, n, P, _ = _run(mod)
+    ref_y, ref_n = O.forward(mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], s)
+    check_norm(n, ref_n, torch.bfloat16)
+    check_close(y, ref_y, torch.bfloat16, f"y {T}x{d_out}")
+    check_close(P, np64(mod["x"]) @ np64(mod["A"]).T, torch.bfloat16, "P")
+
+
+def test_fp32_ragged_widths():
+    say("forward fp32 ragged")
+    mod = synth.custom(70, 100, 5, 33, "f32", 1.25, sigma_B=0.05, seed=2)
+    y, n, P, _ = _run(mod)
+    ref_y, ref_n = O.forward(mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], 1.25)
+    check_norm(n, ref_n, torch.float32)
+    check_close(y, ref_y, torch.float32, "y fp32 ragged")
+
+
+def test_invariant_b_zero_m_equals_n():
+    """B = 0 and m = n: g = 1 exactly and the adapter term is exactly zero,
+    so y is the rounded base product x W^T, whatever A is."""
+    say("forward B=0 m=n")
+    mod = synth.custom(512, 1024, 64, 300, "bf16", 1.0, seed=21)
+    W, A, x = gpu(mod["W"]), gpu(mod["A"]), gpu(mod["x"])
+    B0 = torch.zeros(512, 64, dtype=torch.bfloat16, device="cuda:0")
+    n = D.dora_factored_norm(W, A, B0, 1.0)
+    y1, _, _ = D.dora_forward(x, W, A, B0, n, 1.0)
+    y2, _, _ = D.dora_forward(x, W, torch.randn_like(A), B0, n, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    check_close(y1, np64(mod["x"]) @ np64(mod["W"]).T, torch.bfloat16, "y = x W^T")
+
+
+def test_lora_reduction_and_cached_norm():
+    say("forward m=n LoRA / cached n")
+    mod = synth.custom(384, 768, 32, 200, "bf16", 2.0, seed=22)
+    t = {k: gpu(mod[k]) for k in ("x", "W", "A", "B")}
+    n = D.dora_factored_norm(t["W"], t["A"], t["B"], 2.0)
+    y, n2, _ = D.dora_forward(t["x"], t["W"], t["A"], t["B"], n, 2.0)
+    torch.cuda.synchronize()
+    xx, w, a, b = (np64(mod[k]) for k in ("x", "W", "A", "B"))
+    check_close(y, xx @ w.T + 2.0 * (xx @ a.T) @ b.T, torch.bfloat16, "m = n is LoRA")
+    m = gpu(mod["m"])
+    ya, na, _ = D.dora_forward(t["x"], t["W"], t["A"], t["B"], m, 2.0)
+    yb, nb, _ = D.dora_forward(t["x"], t["W"], t["A"], t["B"], m, 2.0, n_in=na)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(na, nb)
+    assert torch.equal(na, n2)
+
+
+def test_forward_empty_tokens():
+    say("forward T=0")
+    mod = synth.custom(64, 128, 8, 0, "bf16", 1.0, seed=23)
+    y, n, P, _ = _run(mod)
+    assert y.shape == (0, 64)
+    ref = O.norm(mod["W"], mod["A"], mod["B"], 1.0)
+    check_norm(n, ref["n"], torch.bfloat16)
+
+
+def test_forward_deterministic():
+    say("forward determinism")
+    mod = synth.custom(1024, 2048, 128, 513, "bf16", 1.0, seed=24)
+    y1, n1, P1, t = _run(mod)
+    y2, n2, P2 = D.dora_forward(t["x"], t["W"], t["A"], t["B"], t["m"], 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(n1, n2) and torch.equal(P1, P2)
+
+
+def _sampled(shape, x=None, mod=None, seed=0, ntok=48, nrow=48):
+    if mod is None:
+        mod = synth.make_module(shape, seed=seed, with_dy=False)
+    if x is not None:
+        mod = dict(mod, x=x)
+    y, n, P, _ = _run(mod)
+    toks = sample_ids(2, ntok, y.shape[0])
+    rows = sample_ids(3, nrow, y.shape[1])
+    ref_y, ref_n = O.forward(mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], mod["s"],
+                             toks=toks, rows=rows)
+    check_norm(np64(n)[rows], ref_n, torch.bfloat16, f"{shape.name} n")
+    got = y[torch.tensor(toks, device=y.device)][:, torch.tensor(rows, device=y.device)]
+    check_close(got, ref_y, torch.bfloat16, f"{shape.name} y sampled")
+    return y
+
+
+@pytest.mark.parametrize("shape", [synth.SQUARE_R64, synth.SQUARE_R384, synth.TRAIN_R384],
+                         ids=lambda s: s.name)
+def test_full_size_sampled(shape):
+    say("forward full size", shape.name)
+    _sampled(shape)
+
+
+def test_mlp_pair_full_size_sampled():
+    """Up module then down module back to back (the down module's tokens are
+    the up module's GPU output); each is checked against the oracle."""
+    say("forward MLP pair")
+    up, down, x = synth.make_mlp_pair(seed=0)
+    up = dict(up, x=x)
+    y_up = _sampled(synth.MLP_UP, mod=up)
+    down = dict(down, x=y_up.cpu())
+    del y_up
+    torch.cuda.empty_cache()
+    _sampled(synth.MLP_DOWN, mod=down)
