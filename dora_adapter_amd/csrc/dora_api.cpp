@@ -50,40 +50,68 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // ------------------------------------------------------------------ planning
 struct GPlan {
-    int cfg = 0;         // bf16 tile shape index (fp32: unused)
+    int cfg = 0;         // bf16 tile configuration (fp32: unused)
     int BM = 0, BN = 0;
     int splits = 1;
     int64_t sps = 0;     // K steps per split
     int ntn = 0;         // tiles along N
 };
 
-// Choose the tile shape and the split-K count for C[M, N] over `steps`
-// K steps by a small time model: (256-CU waves) x (one workgroup's MFMA or
-// VALU time), plus, for a split, writing and re-reading `part_per_split`
-// fp32 values per split and one extra launch.  A split must keep at least
-// 8 K steps and its partials under 1 GiB.
-GPlan plan_gemm(bool bf16, int64_t M, int64_t N, int64_t steps, int64_t part_per_split)
+// One product C[M, N] = sum_seg op(A) op(B) as the planner sees it.
+struct GemmShape {
+    int64_t M, N;
+    int64_t K[2];
+    int nseg;
+    int layout;   // 0: A, B K-major; 1: B MN-major; 2: both MN-major
+    bool dma_ok;  // direct-to-LDS kernel allowed (K-major, K % 32, operands < 2 GiB)
+};
+
+constexpr int64_t kDmaBytes = 1LL << 31;
+
+// A K-major bf16 operand of `rows` x `K` fits the direct-to-LDS kernel.
+bool dma_operand(int64_t rows, int64_t K)
 {
-    const double cu_flops = bf16 ? 2.5e15 / kCUs * 0.7 : 157.3e12 / kCUs * 0.5;
+    return K % GEMM_DMA_BK == 0 && rows * K * 2 < kDmaBytes;
+}
+
+GemmShape nt_shape(int64_t M, int64_t N, int64_t K)
+{
+    return GemmShape{M, N, {K, 0}, 1, 0, dma_operand(M, K) && dma_operand(N, K)};
+}
+
+// Choose the tile configuration and the split-K count by a small time
+// model: (256-CU waves) x (one workgroup's MFMA or VALU time), plus, for a
+// split, writing and re-reading `part_per_split` fp32 values per split and
+// one extra launch.  A split keeps at least 8 K steps and its partials
+// under 1 GiB.
+GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
+{
+    const double cu_flops = bf16 ? 4.0e12 : 157.3e12 / kCUs * 0.5;
     const double hbm = 5.0e12;
-    const int64_t bk = bf16 ? GEMM_BK : GEMM_F32_BK;
     GPlan best;
     double best_cost = -1.0;
     const int ncfg = bf16 ? gemm_bf16_num_cfgs() : 1;
     for (int c = 0; c < ncfg; ++c) {
-        int BM, BN;
+        int BM, BN, bk;
         float rel;
         if (bf16) {
-            TileCfg t = gemm_bf16_cfg(c);
+            const TileCfg t = gemm_bf16_cfg(c);
+            if (t.dma && (sh.layout != 0 || !sh.dma_ok))
+                continue;
             BM = t.BM;
             BN = t.BN;
+            bk = t.bk;
             rel = t.rel_speed;
         } else {
             BM = GEMM_F32_BM;
             BN = GEMM_F32_BN;
+            bk = GEMM_F32_BK;
             rel = 1.0f;
         }
-        const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        int64_t steps = 0;
+        for (int q = 0; q < sh.nseg; ++q)
+            steps += (sh.K[q] + bk - 1) / bk;
+        const int64_t tiles = ((sh.M + BM - 1) / BM) * ((sh.N + BN - 1) / BN);
         const int64_t zmax = std::min<int64_t>(32, std::max<int64_t>(steps / 8, 1));
         for (int64_t z = 1; z <= zmax; ++z) {
             if (z > 1 && static_cast<double>(z) * part_per_split * 4.0 > (1LL << 30))
@@ -101,17 +129,11 @@ GPlan plan_gemm(bool bf16, int64_t M, int64_t N, int64_t steps, int64_t part_per
                 best.BN = BN;
                 best.splits = static_cast<int>(z);
                 best.sps = sps;
-                best.ntn = static_cast<int>((N + BN - 1) / BN);
+                best.ntn = static_cast<int>((sh.N + BN - 1) / BN);
             }
         }
     }
     return best;
-}
-
-int64_t ksteps(bool bf16, int64_t K)
-{
-    const int64_t bk = bf16 ? GEMM_BK : GEMM_F32_BK;
-    return (K + bk - 1) / bk;
 }
 
 // Workspace carve-up: offsets are computed identically by the size queries
@@ -136,9 +158,9 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, Carve &cv)
 {
     const bool bf = dtype == DORA_BF16;
     NormPlan p;
-    p.g = plan_gemm(bf, r, r, ksteps(bf, d_in), r * r);
-    p.u = plan_gemm(bf, d_out, r, ksteps(bf, d_in), 2 * d_out);
-    p.bg = plan_gemm(bf, d_out, r, (bf ? 2 : 1) * ksteps(bf, r), d_out);
+    p.g = plan_gemm(bf, nt_shape(r, r, d_in), r * r);
+    p.u = plan_gemm(bf, nt_shape(d_out, r, d_in), 2 * d_out);
+    p.bg = plan_gemm(bf, GemmShape{d_out, r, {r, r}, bf ? 2 : 1, 1, false}, d_out);
     const size_t start = cv.off;
     p.o_gpart = cv.take(static_cast<size_t>(p.g.splits) * r * r * 4);
     p.o_gfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);
@@ -157,7 +179,7 @@ struct LinPlan {
 // The base product's plan, shared by dora_forward and dora_linear.
 GPlan plan_base(bool bf, int64_t T, int64_t d_in, int64_t d_out)
 {
-    return plan_gemm(bf, T, d_out, ksteps(bf, d_in), T * d_out);
+    return plan_gemm(bf, nt_shape(T, d_out, d_in), T * d_out);
 }
 
 LinPlan plan_linear(int64_t T, int64_t d_in, int64_t d_out, int dtype)
@@ -168,12 +190,22 @@ LinPlan plan_linear(int64_t T, int64_t d_in, int64_t d_out, int dtype)
     return l;
 }
 
+// Forward: the norm, P = x A^T, then one K-concatenated product
+// [x | s P] [W | B]^T whose fp32 accumulator h = x W^T + s P B^T is stored as
+// (m/n) h by the epilogue (no [T, d_out] intermediate).
 struct FwdPlan {
     NormPlan norm;
-    GPlan base, p, lora;
-    size_t o_P, o_Ppart, o_lora, o_part_lora, o_part_base;
+    GPlan p, fused;
+    size_t o_P, o_Ppart, o_sP, o_part_fused;
     size_t bytes;
 };
+
+GemmShape fused_shape(int64_t T, int64_t d_in, int64_t d_out, int64_t r)
+{
+    return GemmShape{T, d_out, {d_in, r}, 2, 0,
+                     dma_operand(T, d_in) && dma_operand(d_out, d_in) && dma_operand(T, r) &&
+                         dma_operand(d_out, r)};
+}
 
 FwdPlan plan_forward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype)
 {
@@ -181,17 +213,14 @@ FwdPlan plan_forward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtyp
     FwdPlan f;
     Carve cv;
     f.norm = plan_norm(d_out, d_in, r, dtype, cv);
-    f.base = plan_base(bf, T, d_in, d_out);
-    f.p = plan_gemm(bf, T, r, ksteps(bf, d_in), T * r);
-    f.lora = plan_gemm(bf, T, d_out, ksteps(bf, r), T * d_out);
+    f.p = plan_gemm(bf, nt_shape(T, r, d_in), T * r);
+    f.fused = plan_gemm(bf, fused_shape(T, d_in, d_out, r), T * d_out);
     const size_t e = esize(dtype);
     f.o_P = cv.take(static_cast<size_t>(T) * r * e);
     f.o_Ppart = cv.take(f.p.splits > 1 ? static_cast<size_t>(f.p.splits) * T * r * 4 : 0);
-    f.o_lora = cv.take(static_cast<size_t>(T) * d_out * e);
-    f.o_part_lora =
-        cv.take(f.lora.splits > 1 ? static_cast<size_t>(f.lora.splits) * T * d_out * 4 : 0);
-    f.o_part_base =
-        cv.take(f.base.splits > 1 ? static_cast<size_t>(f.base.splits) * T * d_out * 4 : 0);
+    f.o_sP = cv.take(static_cast<size_t>(T) * r * e);
+    f.o_part_fused =
+        cv.take(f.fused.splits > 1 ? static_cast<size_t>(f.fused.splits) * T * d_out * 4 : 0);
     f.bytes = cv.off;
     return f;
 }
@@ -209,10 +238,10 @@ BwdPlan plan_backward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dty
     const bool bf = dtype == DORA_BF16;
     BwdPlan b;
     Carve cv;
-    b.q = plan_gemm(bf, T, r, ksteps(bf, d_out), T * r);
-    b.dx = plan_gemm(bf, T, d_in, ksteps(bf, d_out) + ksteps(bf, r), T * d_in);
-    b.dB = plan_gemm(bf, d_out, r, ksteps(bf, T), d_out * r);
-    b.dA = plan_gemm(bf, r, d_in, ksteps(bf, T), r * d_in);
+    b.q = plan_gemm(bf, GemmShape{T, r, {d_out, 0}, 1, 1, false}, T * r);
+    b.dx = plan_gemm(bf, GemmShape{T, d_in, {d_out, r}, 2, 1, false}, T * d_in);
+    b.dB = plan_gemm(bf, GemmShape{d_out, r, {T, 0}, 1, 2, false}, d_out * r);
+    b.dA = plan_gemm(bf, GemmShape{r, d_in, {T, 0}, 1, 2, false}, r * d_in);
     b.t_chunk = dm_t_chunk(T, d_out);
     b.nchunks = T > 0 ? static_cast<int>((T + b.t_chunk - 1) / b.t_chunk) : 0;
     const size_t e = esize(dtype);
@@ -550,18 +579,43 @@ int dora_forward(const void *x, const void *W, const void *A, const void *B, con
     if (T == 0)
         return DORA_OK;
     void *P = P_out ? P_out : static_cast<void *>(w + p.o_P);
-    void *lora = w + p.o_lora;
-    // 2. base = x W^T, written straight into y.
-    DORA_CHECK(run_store(bf, p.base, seg1(T, d_out, x, d_in, W, d_in, d_in), 0, y, d_out, 1.0f,
-                         reinterpret_cast<float *>(w + p.o_part_base), st, "base x W^T"));
-    // 3. P = x A^T.
+    // 2. P = x A^T (kept for the backward).
     DORA_CHECK(run_store(bf, p.p, seg1(T, r, x, d_in, A, d_in, d_in), 0, P, r, 1.0f,
                          reinterpret_cast<float *>(w + p.o_Ppart), st, "adapter x A^T"));
-    // 4. lora = P B^T.
-    DORA_CHECK(run_store(bf, p.lora, seg1(T, d_out, P, r, B, r, r), 0, lora, d_out, 1.0f,
-                         reinterpret_cast<float *>(w + p.o_part_lora), st, "adapter P B^T"));
-    // 5. y = compose(base, lora) in place.
-    DORA_LAUNCH(launch_compose(bf, y, lora, m, n_out, s, T, d_out, y, st), "compose");
+    // 3. s P as the second K segment's operand (P itself when s = 1).
+    const void *sP = P;
+    if (s != 1.0f) {
+        DORA_LAUNCH(launch_scale(bf, P, s, T * r, w + p.o_sP, st), "scale s P");
+        sP = w + p.o_sP;
+    }
+    // 4. y = (m/n) (x W^T + s P B^T): one K-concatenated product; the epilogue
+    //    applies the magnitude scale in the cancellation-safe form and rounds once.
+    {
+        GemmArgs g = seg1(T, d_out, x, d_in, W, d_in, d_in);
+        g.seg[1] = GemmSeg{sP, r, B, r, r};
+        g.nseg = 2;
+        g.mode = EPI_STORE;
+        g.colm = m;
+        g.coln = n_out;
+        if (p.fused.splits <= 1) {
+            g.out = y;
+            g.ldc = d_out;
+            g.out_f32 = bf ? 0 : 1;
+            DORA_LAUNCH(run_gemm(bf, p.fused, g, 0, false, st), "fused forward product");
+        } else {
+            // split-K: fp32 partials of h; the fixed-order sum applies the
+            // same scale and rounds once
+            float *part = reinterpret_cast<float *>(w + p.o_part_fused);
+            g.colm = g.coln = nullptr;
+            g.out = part;
+            g.ldc = d_out;
+            g.out_f32 = 1;
+            DORA_LAUNCH(run_gemm(bf, p.fused, g, 0, false, st), "fused forward product");
+            DORA_LAUNCH(launch_splitk_reduce(bf, part, p.fused.splits, T, d_out, 1.0f, y, st, m,
+                                             n_out),
+                        "fused forward reduce");
+        }
+    }
     return DORA_OK;
 }
 

@@ -40,6 +40,11 @@ struct GemmArgs {
     int64_t ldc;
     int out_f32;             // 1: fp32 output (split-K partials); 0: kernel dtype
     float alpha;
+    // optional per-column magnitude scale of the store: with colm and coln
+    // set, column n of alpha * C is stored as h + ((colm[n] - coln[n]) /
+    // coln[n]) h, i.e. (m/n) h in the cancellation-safe form
+    const float *colm;
+    const float *coln;
     // EPI_ROWDOT
     const void *E;
     int64_t lde;
@@ -56,14 +61,20 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs &a, int layout, bool rowsq, hipStream_t st);
 
-// Tile shapes of the bf16 MFMA GEMM, indexable by `cfg`.
+// Tile configurations of the bf16 MFMA GEMM, indexable by `cfg`.  Two
+// kernels: the general one (any layout, any K, operands staged through
+// registers, K step 64) and the pipelined direct-to-LDS one (layout 0 only,
+// every segment's K a multiple of 32, each operand under 2 GiB, K step 32).
 struct TileCfg {
     int BM, BN;
-    float rel_speed;  // relative MFMA efficiency of a full tile, for planning
+    int bk;           // K values per step
+    bool dma;         // pipelined direct-to-LDS kernel
+    float rel_speed;  // relative throughput of a full tile, for planning
 };
 int gemm_bf16_num_cfgs();
 TileCfg gemm_bf16_cfg(int cfg);
-constexpr int GEMM_BK = 64;      // bf16 K step
+constexpr int GEMM_BK = 64;      // bf16 K step of the general kernel
+constexpr int GEMM_DMA_BK = 32;  // bf16 K step of the direct-to-LDS kernel
 constexpr int GEMM_F32_BM = 64;  // fp32 VALU tile
 constexpr int GEMM_F32_BN = 64;
 constexpr int GEMM_F32_BK = 16;
@@ -73,8 +84,11 @@ constexpr int GEMM_F32_BK = 16;
 hipError_t launch_compose(int bf16, const void *base, const void *lora, const float *m,
                           const float *n, float s, int64_t T, int64_t d_out, void *y,
                           hipStream_t st);
+// out = alpha * sum_z part[z] (fixed order); with colm/coln set, column n is
+// then scaled as h + ((colm[n] - coln[n]) / coln[n]) h before the rounding.
 hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t M, int64_t N,
-                                float alpha, void *out, hipStream_t st);
+                                float alpha, void *out, hipStream_t st,
+                                const float *colm = nullptr, const float *coln = nullptr);
 hipError_t launch_gram_finalize(int bf16, const float *part, int splits, int64_t r, void *G_out,
                                 hipStream_t st);
 hipError_t launch_norm_finish(const float *base_part, int zb, const float *cross_part, int zc,
@@ -86,6 +100,7 @@ hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const f
 hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, int64_t d_out,
                             float *dm, hipStream_t st);
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st);
+hipError_t launch_scale(int bf16, const void *src, float s, int64_t n, void *dst, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
 
 // dh/dm partial sums: rows of T per chunk and number of chunks.

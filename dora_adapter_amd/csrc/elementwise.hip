@@ -7,7 +7,8 @@
 //                backward (DoRA summary, "Statistical analysis"), one pass
 //                over dy and y with fixed-order partial sums.
 //   small ones   split-K reduction, Gram matrix finalisation (fp32 sum of
-//                split partials, bf16 hi/lo split), the row-norm finish.
+//                split partials, bf16 hi/lo split), the row-norm finish, and
+//                the scaled copy s P of the adapter activations.
 //
 // Streaming layout: a thread owns one group of 8 consecutive columns and a
 // contiguous run of rows, so per-column factors (g - 1, g s) are formed once
@@ -187,14 +188,21 @@ __global__ void dm_finish_kernel(const float *__restrict__ part, int nchunks,
 
 template <typename T>
 __global__ void splitk_reduce_kernel(const float *__restrict__ part, int splits, int64_t MN,
-                                     float alpha, T *__restrict__ out)
+                                     int64_t N, float alpha, T *__restrict__ out,
+                                     const float *__restrict__ colm,
+                                     const float *__restrict__ coln)
 {
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < MN;
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         float acc = 0.f;
         for (int z = 0; z < splits; ++z)
             acc += part[static_cast<int64_t>(z) * MN + e];
-        Vec8<T>::store1(out + e, alpha * acc);
+        float v = alpha * acc;
+        if (colm != nullptr) {
+            const int64_t n = e % N;
+            v = __fmaf_rn((colm[n] - coln[n]) / coln[n], v, v);
+        }
+        Vec8<T>::store1(out + e, v);
     }
 }
 
@@ -250,6 +258,14 @@ __global__ void norm_finish_kernel(const float *__restrict__ bp, int zb, const f
         cross[i] = static_cast<float>(c);
     if (gram)
         gram[i] = static_cast<float>(g);
+}
+
+template <typename T>
+__global__ void scale_kernel(const T *__restrict__ src, float s, int64_t n, T *__restrict__ dst)
+{
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        Vec8<T>::store1(dst + i, s * Vec8<T>::load1(src + i));
 }
 
 __global__ void copy_f32_kernel(const float *__restrict__ src, float *__restrict__ dst, int64_t n)
@@ -358,7 +374,8 @@ hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, i
 }
 
 hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t M, int64_t N,
-                                float alpha, void *out, hipStream_t st)
+                                float alpha, void *out, hipStream_t st, const float *colm,
+                                const float *coln)
 {
     const int64_t MN = M * N;
     if (MN == 0)
@@ -368,12 +385,12 @@ hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t
         blocks = 8192;
     if (bf16)
         hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(EW_THREADS), 0, st, part, splits, MN, alpha,
-                           static_cast<uint16_t *>(out));
+                           dim3(EW_THREADS), 0, st, part, splits, MN, N, alpha,
+                           static_cast<uint16_t *>(out), colm, coln);
     else
         hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(EW_THREADS), 0, st, part, splits, MN, alpha,
-                           static_cast<float *>(out));
+                           dim3(EW_THREADS), 0, st, part, splits, MN, N, alpha,
+                           static_cast<float *>(out), colm, coln);
     return hipGetLastError();
 }
 
@@ -404,6 +421,24 @@ hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t 
     if (n == 0)
         return hipSuccess;
     hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(n)), dim3(EW_THREADS), 0, st, src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale(int bf16, const void *src, float s, int64_t n, void *dst, hipStream_t st)
+{
+    if (n == 0)
+        return hipSuccess;
+    int64_t blocks = (n + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 8192)
+        blocks = 8192;
+    if (bf16)
+        hipLaunchKernelGGL((scale_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(EW_THREADS), 0, st, static_cast<const uint16_t *>(src), s, n,
+                           static_cast<uint16_t *>(dst));
+    else
+        hipLaunchKernelGGL((scale_kernel<float>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(EW_THREADS), 0, st, static_cast<const float *>(src), s, n,
+                           static_cast<float *>(dst));
     return hipGetLastError();
 }
 

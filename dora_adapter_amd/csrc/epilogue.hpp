@@ -68,6 +68,13 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
             for (int q = 0; q < 8; ++q)
                 v[q] = g.alpha * Cs[row * CST + c * 8 + q];
             const int cnt = (N - n) < 8 ? static_cast<int>(N - n) : 8;
+            if (g.colm != nullptr) {
+                // y = h + (g - 1) h with g - 1 = (m - n) / n formed in fp32
+                for (int q = 0; q < cnt; ++q) {
+                    const float mi = g.colm[n + q], ni = g.coln[n + q];
+                    v[q] = __fmaf_rn((mi - ni) / ni, v[q], v[q]);
+                }
+            }
             if (g.out_f32) {
                 float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * M * g.ldc +
                            m * g.ldc + n;

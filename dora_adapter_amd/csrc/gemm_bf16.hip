@@ -28,6 +28,7 @@
 //   * XCD-aware tile order (epilogue.hpp, tile_coords).
 #include "dora_internal.hpp"
 #include "epilogue.hpp"
+#include "gemm_bf16_dma.hpp"
 
 namespace dora {
 namespace {
@@ -301,18 +302,29 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
     }
 }
 
-struct CfgDesc {
-    int BM, BN;
-    float rel;
+// Tile configurations.  rel_speed is the measured throughput of a full tile
+// on the 8192 x 28672 x 8192 base product, relative to the best one.
+constexpr TileCfg kCfgs[] = {
+    {256, 256, GEMM_BK, false, 0.76f},
+    {256, 128, GEMM_BK, false, 0.68f},
+    {128, 128, GEMM_BK, false, 0.56f},
+    {128, 64, GEMM_BK, false, 0.40f},
+    {256, 256, GEMM_DMA_BK, true, 1.00f},  // 8 waves (2 x 4), 4 stages
+    {256, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 4 stages
+    {128, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 4 stages, 2 per CU
 };
-// Tile shapes, largest first.  rel_speed is a planning weight (relative
-// MFMA efficiency of a full tile) used to choose a tile and a split count.
-constexpr CfgDesc kCfgs[] = {
-    {256, 256, 1.00f},
-    {256, 128, 0.90f},
-    {128, 128, 0.75f},
-    {128, 64, 0.55f},
-};
+
+template <int BM, int BN, int WM, int WN, int S, bool RS>
+hipError_t launch_dma(const GemmArgs &a, hipStream_t st)
+{
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    if (tiles == 0 || a.splits == 0)
+        return hipSuccess;
+    dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, S, RS>), grid,
+                       dim3(WM * WN * 64), 0, st, a);
+    return hipGetLastError();
+}
 
 template <int BM, int BN, bool AK, bool BKM, bool RS>
 hipError_t launch_one(const GemmArgs &a, hipStream_t st)
@@ -350,7 +362,7 @@ int gemm_bf16_num_cfgs()
 
 TileCfg gemm_bf16_cfg(int cfg)
 {
-    return TileCfg{kCfgs[cfg].BM, kCfgs[cfg].BN, kCfgs[cfg].rel};
+    return kCfgs[cfg];
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, hipStream_t st)
@@ -366,6 +378,19 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
         return launch_cfg<128, 128>(a, layout, rowsq, st);
     case 3:
         return launch_cfg<128, 64>(a, layout, rowsq, st);
+    case 4:
+    case 5:
+    case 6:
+        if (layout != 0)
+            return hipErrorInvalidValue;
+        if (cfg == 4)
+            return rowsq ? launch_dma<256, 256, 2, 4, 4, true>(a, st)
+                         : launch_dma<256, 256, 2, 4, 4, false>(a, st);
+        if (cfg == 5)
+            return rowsq ? launch_dma<256, 128, 2, 2, 4, true>(a, st)
+                         : launch_dma<256, 128, 2, 2, 4, false>(a, st);
+        return rowsq ? launch_dma<128, 128, 2, 2, 4, true>(a, st)
+                     : launch_dma<128, 128, 2, 2, 4, false>(a, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -127,10 +127,16 @@ int dora_compose(const void *base, const void *lora, const float *m, const float
 /*
  * dora_forward - the DoRA module forward ([SD], [DoRA]):
  *     n   = factored row norm (as dora_factored_norm), unless n_in is given
- *     y   = x W^T                            (base, written into y)
  *     P   = x A^T                            [T, r]
- *     lra = P B^T                            [T, d_out], in the workspace
- *     y   = compose(y, lra, m, n, s)         (as dora_compose, in place)
+ *     h   = x W^T + (s P) B^T                one K-concatenated product,
+ *                                            accumulated in fp32
+ *     y   = h + ((m - n) / n) h              = (m/n) h, applied by the
+ *                                            product's epilogue, rounded once
+ *   The base and adapter products share one accumulator, so the composition
+ *   happens in the same pass that produces them ([SD]'s single-pass compose,
+ *   taken one step further): no [T, d_out] intermediate exists.  s P is
+ *   rounded to the element type before the product (exact when s = 1 or a
+ *   power of two).
  *   x [T, d_in], W [d_out, d_in], A [r, d_in], B [d_out, r] in `dtype`;
  *   m [d_out] fp32.  y [T, d_out] in `dtype` (output).
  *   n_out [d_out] fp32: receives n (required; with n_in it receives a copy).
