@@ -68,10 +68,16 @@ struct GemmShape {
 
 constexpr int64_t kDmaBytes = 1LL << 31;
 
-// A K-major bf16 operand of `rows` x `K` fits the direct-to-LDS kernel.
+// Operands the direct-to-LDS kernel can take (bf16, byte offsets < 2 GiB):
+// a K-major one of `rows` x `K` needs whole 32-wide K steps; an MN-major one
+// ([K][ld]) loads its K tail as zeros but addresses up to 32 rows past K.
 bool dma_operand(int64_t rows, int64_t K)
 {
     return K % GEMM_DMA_BK == 0 && rows * K * 2 < kDmaBytes;
+}
+bool dma_mn_operand(int64_t K, int64_t ld)
+{
+    return (K + GEMM_DMA_BK) * ld * 2 < kDmaBytes;
 }
 
 GemmShape nt_shape(int64_t M, int64_t N, int64_t K)
@@ -96,7 +102,7 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
         float rel;
         if (bf16) {
             const TileCfg t = gemm_bf16_cfg(c);
-            if (t.dma && (sh.layout != 0 || !sh.dma_ok))
+            if (t.dma && !sh.dma_ok)
                 continue;
             BM = t.BM;
             BN = t.BN;
@@ -160,7 +166,9 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, Carve &cv)
     NormPlan p;
     p.g = plan_gemm(bf, nt_shape(r, r, d_in), r * r);
     p.u = plan_gemm(bf, nt_shape(d_out, r, d_in), 2 * d_out);
-    p.bg = plan_gemm(bf, GemmShape{d_out, r, {r, r}, bf ? 2 : 1, 1, false}, d_out);
+    p.bg = plan_gemm(bf, GemmShape{d_out, r, {r, r}, bf ? 2 : 1, 1,
+                                   dma_operand(d_out, r) && dma_mn_operand(r, r)},
+                     d_out);
     const size_t start = cv.off;
     p.o_gpart = cv.take(static_cast<size_t>(p.g.splits) * r * r * 4);
     p.o_gfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);
@@ -238,10 +246,19 @@ BwdPlan plan_backward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dty
     const bool bf = dtype == DORA_BF16;
     BwdPlan b;
     Carve cv;
-    b.q = plan_gemm(bf, GemmShape{T, r, {d_out, 0}, 1, 1, false}, T * r);
-    b.dx = plan_gemm(bf, GemmShape{T, d_in, {d_out, r}, 2, 1, false}, T * d_in);
-    b.dB = plan_gemm(bf, GemmShape{d_out, r, {T, 0}, 1, 2, false}, d_out * r);
-    b.dA = plan_gemm(bf, GemmShape{r, d_in, {T, 0}, 1, 2, false}, r * d_in);
+    b.q = plan_gemm(bf, GemmShape{T, r, {d_out, 0}, 1, 1,
+                                  dma_operand(T, d_out) && dma_mn_operand(d_out, r)},
+                    T * r);
+    b.dx = plan_gemm(bf, GemmShape{T, d_in, {d_out, r}, 2, 1,
+                                   dma_operand(T, d_out) && dma_mn_operand(d_out, d_in) &&
+                                       dma_operand(T, r) && dma_mn_operand(r, d_in)},
+                     T * d_in);
+    b.dB = plan_gemm(bf, GemmShape{d_out, r, {T, 0}, 1, 2,
+                                   dma_mn_operand(T, d_out) && dma_mn_operand(T, r)},
+                     d_out * r);
+    b.dA = plan_gemm(bf, GemmShape{r, d_in, {T, 0}, 1, 2,
+                                   dma_mn_operand(T, r) && dma_mn_operand(T, d_in)},
+                     r * d_in);
     b.t_chunk = dm_t_chunk(T, d_out);
     b.nchunks = T > 0 ? static_cast<int>((T + b.t_chunk - 1) / b.t_chunk) : 0;
     const size_t e = esize(dtype);

@@ -62,9 +62,9 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
 hipError_t launch_gemm_f32(const GemmArgs &a, int layout, bool rowsq, hipStream_t st);
 
 // Tile configurations of the bf16 MFMA GEMM, indexable by `cfg`.  Two
-// kernels: the general one (any layout, any K, operands staged through
-// registers, K step 64) and the pipelined direct-to-LDS one (layout 0 only,
-// every segment's K a multiple of 32, each operand under 2 GiB, K step 32).
+// kernels: the general one (any shape, operands staged through registers, K
+// step 64) and the pipelined direct-to-LDS one (K step 32; K-major operands
+// need K % 32 == 0, and every operand must stay under 2 GiB).
 struct TileCfg {
     int BM, BN;
     int bk;           // K values per step

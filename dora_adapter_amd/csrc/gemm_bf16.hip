@@ -314,16 +314,53 @@ constexpr TileCfg kCfgs[] = {
     {128, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 4 stages, 2 per CU
 };
 
-template <int BM, int BN, int WM, int WN, int S, bool RS>
+}  // namespace
+
+// Explicit instantiations of the pipelined kernels: with implicit
+// instantiation from the launchers alone, the host compiler emitted launch
+// stubs for only some of them.
+#define DORA_DMA_INST(BM, BN, WM, WN)                                                       \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, true, true, true>(  \
+        GemmArgs);                                                                         \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, true, true, false>( \
+        GemmArgs);                                                                         \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, true, false, false>(\
+        GemmArgs);                                                                         \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, false, false, false>(\
+        GemmArgs);
+DORA_DMA_INST(256, 256, 2, 4)
+DORA_DMA_INST(256, 128, 2, 2)
+DORA_DMA_INST(128, 128, 2, 2)
+#undef DORA_DMA_INST
+
+namespace {
+
+template <int BM, int BN, int WM, int WN, int S, bool AK, bool BKM, bool RS>
 hipError_t launch_dma(const GemmArgs &a, hipStream_t st)
 {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles == 0 || a.splits == 0)
         return hipSuccess;
     dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
-    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, S, RS>), grid,
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, S, AK, BKM, RS>), grid,
                        dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStream_t st)
+{
+    switch (layout) {
+    case 0:
+        return rowsq ? launch_dma<BM, BN, WM, WN, 4, true, true, true>(a, st)
+                     : launch_dma<BM, BN, WM, WN, 4, true, true, false>(a, st);
+    case 1:
+        return launch_dma<BM, BN, WM, WN, 4, true, false, false>(a, st);
+    case 2:
+        return launch_dma<BM, BN, WM, WN, 4, false, false, false>(a, st);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 template <int BM, int BN, bool AK, bool BKM, bool RS>
@@ -379,18 +416,11 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
     case 3:
         return launch_cfg<128, 64>(a, layout, rowsq, st);
     case 4:
+        return launch_dma_layout<256, 256, 2, 4>(a, layout, rowsq, st);
     case 5:
+        return launch_dma_layout<256, 128, 2, 2>(a, layout, rowsq, st);
     case 6:
-        if (layout != 0)
-            return hipErrorInvalidValue;
-        if (cfg == 4)
-            return rowsq ? launch_dma<256, 256, 2, 4, 4, true>(a, st)
-                         : launch_dma<256, 256, 2, 4, 4, false>(a, st);
-        if (cfg == 5)
-            return rowsq ? launch_dma<256, 128, 2, 2, 4, true>(a, st)
-                         : launch_dma<256, 128, 2, 2, 4, false>(a, st);
-        return rowsq ? launch_dma<128, 128, 2, 2, 4, true>(a, st)
-                     : launch_dma<128, 128, 2, 2, 4, false>(a, st);
+        return launch_dma_layout<128, 128, 2, 2>(a, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }
