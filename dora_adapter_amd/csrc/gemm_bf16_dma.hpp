@@ -110,6 +110,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void *base,
                                              0x00020000);
 }
 
+// One direct-to-LDS load: lane l's 16 bytes at rsrc + voff + soff land at LDS
+// byte lds + 16 l.  Issued from inline asm (no register outputs; it clobbers
+// m0 and memory) rather than the builtin: the compiler treats the builtin as
+// an LDS store and then drains every such load (vmcnt(0)) before any
+// transpose read it cannot prove disjoint, which would empty the pipeline
+// each step.  Completion is covered by the kernel's explicit vmcnt waits and
+// barriers.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff,
+                                          uint32_t soff)
+{
+    __asm__ volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+                     : "memory", "m0");
+}
+
 // One operand's DMA plan: per-lane byte offsets of the sources of the
 // wave's load instructions, computed once per tile.
 //   K-major (rows = M or N, ld over K): instruction i fills 16 tile rows;
@@ -156,13 +172,15 @@ struct OperandDma {
                                           int64_t k0, int64_t ld, int wave) const
     {
         const uint32_t kadd = static_cast<uint32_t>(KMAJ ? k0 * 2 : k0 * ld * 2);
+        const uint32_t base = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((lds_void *)(dst + wave * 1024)));
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            lds_void *d = (lds_void *)(dst + (i * NW + wave) * 1024);
+            const uint32_t lds = __builtin_amdgcn_readfirstlane(base + i * NW * 1024);
             if constexpr (KMAJ)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, off[i], kadd, 0, 0);
+                lds_dma16(rsrc, lds, off[i], kadd);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, d, 16, off[i] + kadd, 0, 0, 0);
+                lds_dma16(rsrc, lds, off[i] + kadd, 0u);
         }
     }
 };
