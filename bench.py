@@ -46,7 +46,7 @@ def kernel_source_hash():
     """Hash of the GEMM kernel sources: counter readings are only reused for
     the kernel they were taken on."""
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "epilogue.hpp", "dora_internal.hpp"):
+    for f in ("gemm_bf16.hip", "gemm_bf16_dma.hpp", "epilogue.hpp", "dora_internal.hpp"):
         with open(os.path.join(ROOT, "dora_adapter_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
