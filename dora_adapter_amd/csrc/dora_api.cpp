@@ -63,17 +63,20 @@ struct GemmShape {
     int64_t K[2];
     int nseg;
     int layout;   // 0: A, B K-major; 1: B MN-major; 2: both MN-major
-    bool dma_ok;  // direct-to-LDS kernel allowed (K-major, K % 32, operands < 2 GiB)
+    bool dma_ok;  // direct-to-LDS kernel allowed (K-major K % 8, operands < 2 GiB)
 };
 
-constexpr int64_t kDmaBytes = 1LL << 31;
+// Byte offsets of the direct-to-LDS kernel are 32-bit and carry a bias of
+// up to 3 KiB (grouped loads); keep every operand's range below 2 GiB - 4 KiB.
+constexpr int64_t kDmaBytes = (1LL << 31) - 4096;
 
 // Operands the direct-to-LDS kernel can take (bf16, byte offsets < 2 GiB):
-// a K-major one of `rows` x `K` needs whole 32-wide K steps; an MN-major one
-// ([K][ld]) loads its K tail as zeros but addresses up to 32 rows past K.
+// a K-major one of `rows` x `K` loads whole 16-byte chunks (K % 8) and zeros
+// past K; an MN-major one ([K][ld]) loads its K tail as zeros but addresses
+// up to one stage (64 rows) past K.
 bool dma_operand(int64_t rows, int64_t K)
 {
-    return K % GEMM_DMA_BK == 0 && rows * K * 2 < kDmaBytes;
+    return K % 8 == 0 && rows * K * 2 < kDmaBytes;
 }
 bool dma_mn_operand(int64_t K, int64_t ld)
 {

@@ -63,8 +63,8 @@ hipError_t launch_gemm_f32(const GemmArgs &a, int layout, bool rowsq, hipStream_
 
 // Tile configurations of the bf16 MFMA GEMM, indexable by `cfg`.  Two
 // kernels: the general one (any shape, operands staged through registers, K
-// step 64) and the pipelined direct-to-LDS one (K step 32; K-major operands
-// need K % 32 == 0, and every operand must stay under 2 GiB).
+// step 64) and the pipelined direct-to-LDS one (K stage 64; K-major operands
+// need K % 8 == 0, and every operand must stay under 2 GiB).
 struct TileCfg {
     int BM, BN;
     int bk;           // K values per step
@@ -74,7 +74,7 @@ struct TileCfg {
 int gemm_bf16_num_cfgs();
 TileCfg gemm_bf16_cfg(int cfg);
 constexpr int GEMM_BK = 64;      // bf16 K step of the general kernel
-constexpr int GEMM_DMA_BK = 32;  // bf16 K step of the direct-to-LDS kernel
+constexpr int GEMM_DMA_BK = 64;  // bf16 K stage of the direct-to-LDS kernel
 constexpr int GEMM_F32_BM = 64;  // fp32 VALU tile
 constexpr int GEMM_F32_BN = 64;
 constexpr int GEMM_F32_BK = 16;

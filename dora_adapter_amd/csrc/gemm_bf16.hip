@@ -309,9 +309,9 @@ constexpr TileCfg kCfgs[] = {
     {256, 128, GEMM_BK, false, 0.68f},
     {128, 128, GEMM_BK, false, 0.56f},
     {128, 64, GEMM_BK, false, 0.40f},
-    {256, 256, GEMM_DMA_BK, true, 1.00f},  // 8 waves (2 x 4), 4 stages
-    {256, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 4 stages
-    {128, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 4 stages, 2 per CU
+    {256, 256, GEMM_DMA_BK, true, 1.00f},  // 4 waves (2 x 2), 128 x 128 per wave
+    {256, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2)
+    {128, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 2 per CU
 };
 
 }  // namespace
@@ -319,30 +319,28 @@ constexpr TileCfg kCfgs[] = {
 // Explicit instantiations of the pipelined kernels: with implicit
 // instantiation from the launchers alone, the host compiler emitted launch
 // stubs for only some of them.
-#define DORA_DMA_INST(BM, BN, WM, WN)                                                       \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, true, true, true>(  \
-        GemmArgs);                                                                         \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, true, true, false>( \
-        GemmArgs);                                                                         \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, true, false, false>(\
-        GemmArgs);                                                                         \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, 4, false, false, false>(\
+#define DORA_DMA_INST(BM, BN, WM, WN)                                                          \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, true, true>(GemmArgs);  \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, true, false>(GemmArgs); \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, false, false>(         \
+        GemmArgs);                                                                                \
+    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, false, false, false>(        \
         GemmArgs);
-DORA_DMA_INST(256, 256, 2, 4)
+DORA_DMA_INST(256, 256, 2, 2)
 DORA_DMA_INST(256, 128, 2, 2)
 DORA_DMA_INST(128, 128, 2, 2)
 #undef DORA_DMA_INST
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int S, bool AK, bool BKM, bool RS>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
 hipError_t launch_dma(const GemmArgs &a, hipStream_t st)
 {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles == 0 || a.splits == 0)
         return hipSuccess;
     dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
-    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, S, AK, BKM, RS>), grid,
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, AK, BKM, RS>), grid,
                        dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
 }
@@ -352,12 +350,12 @@ hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStrea
 {
     switch (layout) {
     case 0:
-        return rowsq ? launch_dma<BM, BN, WM, WN, 4, true, true, true>(a, st)
-                     : launch_dma<BM, BN, WM, WN, 4, true, true, false>(a, st);
+        return rowsq ? launch_dma<BM, BN, WM, WN, true, true, true>(a, st)
+                     : launch_dma<BM, BN, WM, WN, true, true, false>(a, st);
     case 1:
-        return launch_dma<BM, BN, WM, WN, 4, true, false, false>(a, st);
+        return launch_dma<BM, BN, WM, WN, true, false, false>(a, st);
     case 2:
-        return launch_dma<BM, BN, WM, WN, 4, false, false, false>(a, st);
+        return launch_dma<BM, BN, WM, WN, false, false, false>(a, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -416,7 +414,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
     case 3:
         return launch_cfg<128, 64>(a, layout, rowsq, st);
     case 4:
-        return launch_dma_layout<256, 256, 2, 4>(a, layout, rowsq, st);
+        return launch_dma_layout<256, 256, 2, 2>(a, layout, rowsq, st);
     case 5:
         return launch_dma_layout<256, 128, 2, 2>(a, layout, rowsq, st);
     case 6:

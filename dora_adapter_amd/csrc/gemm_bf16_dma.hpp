@@ -5,37 +5,50 @@
 // or N contiguous: W and A in dh W, dh and P in dh^T P, Q and x in Q^T x).
 //
 //   * v_mfma_f32_32x32x16_bf16: one wavefront keeps the matrix core busy
-//     from only a few independent accumulators (the 16x16x32 shape needs
-//     many more chains and several waves per SIMD to reach the same rate).
+//     from a few independent accumulators, so a workgroup of four waves
+//     (one per SIMD) can hold a 128 x 128 wave tile in accumulation
+//     registers, which halves LDS fragment traffic per flop against eight
+//     waves of 128 x 64.
 //   * Operand tiles move global -> LDS with direct-to-LDS buffer loads
 //     (buffer_load_dwordx4 ... lds): no VGPR staging, asynchronous, landing
 //     in LDS in lane order (lane l writes bytes [16 l, 16 l + 16) of a 1 KiB
 //     block); each lane fetches the global 16-byte chunk that belongs at its
 //     LDS position.
-//   * K-major tiles are rows of 32 K values (64 bytes), chunk c of row r at
-//     slot c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3 & 1)) & 3; fragments are read
-//     with ds_read_b128 (8 and 16 consecutive rows hit distinct banks).
-//   * MN-major tiles are 32 rows (one per K value) of R M or N values; the
+//   * A stage holds BK = 64 K values.  K-major tile rows are then 128 bytes,
+//     one full L2 line per row and load (32-wide rows would issue twice as
+//     many 64-byte requests for the same bytes).  Chunk c of row r sits at
+//     slot c ^ g(r), g(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7, so that the 16
+//     rows of a 16-lane ds_read_b128 phase, and any 8 consecutive rows, hit
+//     distinct banks.
+//   * MN-major tiles are 64 rows (one per K value) of R M or N values; the
 //     16-byte chunk c of row k sits at c ^ t(k), t(k) = {0, 6, 10, 12}[k & 3].
 //     Fragments are read with two ds_read_b64_tr_b16: within each group of
 //     16 lanes, lane j reads 4 consecutive values of row k0 + j / 4 at column
 //     c0 + 4 (j % 4), and lane i receives column c0 + i of rows k0 .. k0 + 3,
 //     exactly half of an MFMA fragment.  t keeps the 4 rows x 32 bytes of a
 //     16-lane group (and the 4 rows x 64 bytes of two groups) on distinct
-//     banks.  K rows past the end fall outside the buffer range and load as
-//     zeros, so K need not be a multiple of 32 for MN-major operands.
-//   * STAGES steps of BK = 32 are resident: step s + STAGES - 1 is issued
-//     right after the barrier of step s.  After that barrier (which also
-//     makes step s + 1 visible) each wave reads its fragments of step s + 1
-//     and then runs the MFMAs of step s from registers.  One barrier per step.
-//   * Rows / columns past M or N load clamped, valid data (never stored); the
-//     host checks K % 32 for K-major operands and that every operand is under
-//     2 GiB (32-bit buffer offsets).
+//     banks.
+//   * K past the end of a segment loads as zeros: an MN-major operand's rows
+//     past K fall outside its buffer range; a K-major lane whose chunk lies
+//     past K is given an out-of-range offset.  Rows / columns past M or N
+//     load clamped, valid data (never stored).  The host checks that every
+//     operand is under 2 GiB (32-bit buffer offsets) and that K-major K is a
+//     multiple of 8 (whole 16-byte chunks).
+//   * Two stage slots (2 x 64 KiB at 256 x 256).  Each stage runs as two
+//     32-wide halves: while the MFMAs of one half run from registers, the
+//     wave reads the fragments of the next half into the other register
+//     set.  Half 1 of stage D starts with the only barrier of the stage: it
+//     makes stage D + 1 visible and frees slot D (its fragments are all in
+//     registers by then), and the loads of stage D + 2 go there.  A load thus
+//     has two halves of MFMA time to land.
 //   * The epilogue is the shared LDS-staged one (epilogue.hpp).
 #pragma once
 
 #include "dora_internal.hpp"
 #include "epilogue.hpp"
+
+#include <type_traits>
+#include <utility>
 
 namespace dora {
 namespace dma {
@@ -44,12 +57,27 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BK = 32;          // K values per step (64 bytes per tile row)
-constexpr int ROW_BYTES = BK * 2;
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N - 1>).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
-// Depends on the low 4 bits of r only, so a 16-row DMA block (whose first row
-// is a multiple of 16) can compute it from the row within the block.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+constexpr int BK = GEMM_DMA_BK;  // K values per stage
+static_assert(BK == 64, "tile layouts below assume 64 K values per stage");
+constexpr int ROW_BYTES = BK * 2;  // K-major tile row
+
+// K-major chunk slot permutation; depends on the low 4 bits of r only.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+// Chunk swizzle of MN-major tiles: t(k) = {0, 6, 10, 12}[k & 3].
+__device__ __forceinline__ int swz_mn(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
@@ -69,9 +97,9 @@ __device__ __forceinline__ void wait_lgkm0()
 // Workgroup barrier without the release/acquire fences of __syncthreads(),
 // which would wait for every outstanding direct-to-LDS load (vmcnt(0)) and
 // so drain the pipeline.  Before it each wave waits (wait_vmcnt) for its own
-// loads of the step about to be read; its LDS reads of older steps were
-// consumed by MFMAs, hence complete.  The empty asm statements keep the
-// compiler from moving memory accesses across the barrier.
+// loads of the stage about to be read; its LDS reads of the slot about to be
+// refilled were consumed by MFMAs, hence complete.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void stage_barrier()
 {
     __asm__ volatile("" ::: "memory");
@@ -79,108 +107,129 @@ __device__ __forceinline__ void stage_barrier()
     __asm__ volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN>
 struct DmaCfg {
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
-    static constexpr int A_BYTES = BM * ROW_BYTES;
+    static constexpr int A_BYTES = BM * ROW_BYTES;  // also [BK][BM] for MN-major
     static constexpr int B_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int OPS = STAGES * STAGE_BYTES;
+    static constexpr int OPS = 2 * STAGE_BYTES;
     static constexpr int CST = BN + 4;
     static constexpr int EPI = (BM / WM) * CST * 4;
     static constexpr int SMEM = OPS > EPI ? OPS : EPI;
-    // 1 KiB (16-row) blocks per operand tile, and DMA instructions per wave
-    static constexpr int A_BLK = BM / 16, B_BLK = BN / 16;
-    static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "blocks must split over wavefronts");
-    static constexpr int LPW = (A_BLK + B_BLK) / NW;
-    static_assert(STAGES >= 3, "fragment prefetch needs at least 3 stages");
+    // 1 KiB load instructions per operand tile and per wave and stage
+    static constexpr int A_INST = A_BYTES / 1024, B_INST = B_BYTES / 1024;
+    static_assert(A_INST % NW == 0 && B_INST % NW == 0, "tile loads must split over wavefronts");
+    static constexpr int LPS = (A_INST + B_INST) / NW;
+    static_assert(LPS < 64, "vmcnt range");
 };
 
-// Chunk swizzle of MN-major tiles: t(k) = {0, 6, 10, 12}[k & 3].
-__device__ __forceinline__ int swz_mn(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
-
-// Buffer descriptor over one operand matrix (raw, byte-addressed; dword 3 =
-// 0x00020000 selects plain linear addressing on gfx9-family parts).  Loads
-// at offsets >= `bytes` return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void *base, int64_t bytes)
+// Byte range of an operand buffer, capped to the 31 bits a descriptor
+// range takes here.
+__device__ __forceinline__ int range_bytes(int64_t bytes)
 {
-    const int nrec = bytes < 0x7fffffff ? static_cast<int>(bytes) : 0x7fffffff;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), nrec,
-                                             0x00020000);
+    return bytes < 0x7fffffff ? static_cast<int>(bytes) : 0x7fffffff;
 }
 
-// One direct-to-LDS load: lane l's 16 bytes at rsrc + voff + soff land at LDS
-// byte lds + 16 l.  Issued from inline asm (no register outputs; it clobbers
-// m0 and memory) rather than the builtin: the compiler treats the builtin as
-// an LDS store and then drains every such load (vmcnt(0)) before any
-// transpose read it cannot prove disjoint, which would empty the pipeline
-// each step.  Completion is covered by the kernel's explicit vmcnt waits and
-// barriers.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff,
-                                          uint32_t soff)
+// Loads go out in groups of four whose LDS destinations are consecutive
+// 1 KiB blocks: the instruction offset (0, 1024, 2048, 3072) advances the
+// LDS address and the global address alike, so m0 is written once per group.
+// (An m0 write waits for the previous direct-to-LDS load to take its m0, so
+// one write per load stalls the issuing wave, and with it the matrix core.)
+// Per-lane offsets are pre-reduced by the instruction offset and raised by
+// GROUP_BIAS, and the descriptor base is lowered by GROUP_BIAS, which keeps
+// every offset non-negative.
+constexpr int GROUP = 4;
+constexpr uint32_t GROUP_BIAS = (GROUP - 1) * 1024;
+
+// Buffer descriptor over one operand matrix (raw, byte-addressed; dword 3 =
+// 0x00020000 selects plain linear addressing on gfx9-family parts), with its
+// base lowered by GROUP_BIAS.  Loads at (biased) offsets past the range
+// return zeros; the range check includes the instruction offset.  An empty
+// range (`bytes` = 0) makes every load return zeros.  The base and range
+// pass through readfirstlane so the descriptor is built in scalar registers
+// even where it is chosen per stage.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void *base, int bytes)
 {
-    __asm__ volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+    const uint64_t p = reinterpret_cast<uint64_t>(base) - GROUP_BIAS;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+    const int64_t biased = bytes > 0 ? static_cast<int64_t>(bytes) + GROUP_BIAS : 0;
+    const int nrec = __builtin_amdgcn_readfirstlane(
+        static_cast<int>(biased < 0x7fffffff ? biased : 0x7fffffff));
+    void *q = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, static_cast<short>(0), nrec, 0x00020000);
+}
+
+// One group of direct-to-LDS loads: instruction j moves lane l's 16 bytes at
+// rsrc + v[j] + soff + 1024 j to LDS byte lds + 1024 j + 16 l.  Issued from
+// inline asm (no register outputs; it clobbers m0 and memory) rather than
+// the builtin: the compiler treats the builtin as an LDS store and then
+// drains every such load (vmcnt(0)) before any transpose read it cannot
+// prove disjoint, which would empty the pipeline each step.  Completion is
+// covered by the kernel's explicit vmcnt waits and barriers.
+__device__ __forceinline__ void lds_dma16x4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t v0,
+                                            uint32_t v1, uint32_t v2, uint32_t v3, uint32_t soff)
+{
+    static_assert(GROUP == 4, "one asm statement per four loads");
+    __asm__ volatile("s_mov_b32 m0, %4\n\t"
+                     "s_nop 0\n\t"
+                     "buffer_load_dwordx4 %0, %5, %6 offen lds\n\t"
+                     "buffer_load_dwordx4 %1, %5, %6 offen offset:1024 lds\n\t"
+                     "buffer_load_dwordx4 %2, %5, %6 offen offset:2048 lds\n\t"
+                     "buffer_load_dwordx4 %3, %5, %6 offen offset:3072 lds"
                      :
-                     : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+                     : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(lds), "s"(rsrc), "s"(soff)
                      : "memory", "m0");
 }
 
-// One operand's DMA plan: per-lane byte offsets of the sources of the
-// wave's load instructions, computed once per tile.
-//   K-major (rows = M or N, ld over K): instruction i fills 16 tile rows;
-//   lane l fetches row l >> 2 of the block and the K chunk that belongs at
-//   slot l & 3.  A step adds its K offset as the scalar buffer offset.
-//   MN-major (rows = K, ld over M or N): instruction i fills 1 KiB of the
-//   [32][R] tile; lane l fetches the chunk that belongs at byte 16 l.  A step
-//   adds k0 * ld * 2 to the per-lane offset (rows past K are out of range
-//   and load as zeros).
+constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor range
+
+// One operand's load plan: per-lane byte offsets (biased, see GROUP_BIAS)
+// of the sources of the wave's load instructions, computed once per tile.
+// Wave w fills the PER consecutive 1 KiB blocks from w * PER.
+//   K-major (rows = M or N, ld over K): a block holds 8 tile rows; lane l
+//   fetches row l >> 3 of the block and the K chunk that belongs at slot
+//   l & 7 (kch[i]: its first K index within the stage).  A stage adds its K
+//   offset as the scalar buffer offset.
+//   MN-major (rows = K, ld over M or N): a block is 1 KiB of the [64][R]
+//   tile; lane l fetches the chunk that belongs at byte 16 l.  A stage adds
+//   k0 * ld * 2 to the per-lane offset (rows past K are out of range and
+//   load as zeros).
 template <bool KMAJ, int R, int NW>
 struct OperandDma {
-    static constexpr int NINST = R / 16;  // 1 KiB load instructions per tile
+    static constexpr int NINST = R * ROW_BYTES / 1024;
     static_assert(NINST % NW == 0, "tile loads must split over wavefronts");
     static constexpr int PER = NINST / NW;
-    static constexpr int PITCH = R * 2;   // MN-major row bytes
+    static_assert(PER % GROUP == 0, "whole load groups per wave");
+    static constexpr int PITCH = R * 2;  // MN-major row bytes
     static_assert(KMAJ || R >= 128, "MN-major tiles need >= 16 chunks per row");
     uint32_t off[PER];
+    uint32_t kch[KMAJ ? PER : 1];
 
     __device__ __forceinline__ void init(int64_t mn_extent, int64_t ld, int64_t mn0, int wave,
                                          int lane)
     {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int blk = i * NW + wave;
+            const int blk = wave * PER + i;
+            const uint32_t bias = GROUP_BIAS - (i % GROUP) * 1024;
             if constexpr (KMAJ) {
-                const int rloc = lane >> 2;
-                const int chunk = (lane & 3) ^ swz(rloc);
-                int64_t row = mn0 + blk * 16 + rloc;
+                const int rloc = blk * 8 + (lane >> 3);
+                const int chunk = (lane & 7) ^ swz(rloc);
+                int64_t row = mn0 + rloc;
                 row = row < mn_extent ? row : mn_extent - 1;
-                off[i] = static_cast<uint32_t>((row * ld + chunk * 8) * 2);
+                off[i] = static_cast<uint32_t>((row * ld + chunk * 8) * 2) + bias;
+                kch[i] = static_cast<uint32_t>(chunk * 8);
             } else {
                 const int b = blk * 1024 + lane * 16;
                 const int krow = b / PITCH;
                 const int chunk = ((b % PITCH) >> 4) ^ swz_mn(krow);
                 int64_t col = mn0 + chunk * 8;
                 col = col + 8 <= mn_extent ? col : mn_extent - 8;
-                off[i] = static_cast<uint32_t>((krow * ld + col) * 2);
+                off[i] = static_cast<uint32_t>((krow * ld + col) * 2) + bias;
             }
-        }
-    }
-
-    // Issue the tile's loads of the step whose first K index is k0.
-    __device__ __forceinline__ void issue(unsigned char *dst, __amdgpu_buffer_rsrc_t rsrc,
-                                          int64_t k0, int64_t ld, int wave) const
-    {
-        const uint32_t kadd = static_cast<uint32_t>(KMAJ ? k0 * 2 : k0 * ld * 2);
-        const uint32_t base = static_cast<uint32_t>(
-            reinterpret_cast<uintptr_t>((lds_void *)(dst + wave * 1024)));
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const uint32_t lds = __builtin_amdgcn_readfirstlane(base + i * NW * 1024);
-            if constexpr (KMAJ)
-                lds_dma16(rsrc, lds, off[i], kadd);
-            else
-                lds_dma16(rsrc, lds, off[i] + kadd, 0u);
         }
     }
 };
@@ -190,20 +239,20 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 // The MFMA fragment of 32 M (or N) indices starting at `mn` and the 8 K
-// values 16 kk + 8 (lane >> 5) + 0..7 of a step: lane holds index
-// mn + (lane & 31).
+// values 16 q + 8 (lane >> 5) + 0..7 of a stage (q = 0..3): lane holds
+// index mn + (lane & 31).
 template <bool KMAJ, int R>
-__device__ __forceinline__ bf16x8_t read_frag(const unsigned char *tile, int mn, int kk, int lane)
+__device__ __forceinline__ bf16x8_t read_frag(const unsigned char *tile, int mn, int q, int lane)
 {
     if constexpr (KMAJ) {
         const int row = mn + (lane & 31);
-        const int fc = kk * 2 + (lane >> 5);
+        const int fc = q * 2 + (lane >> 5);
         return *reinterpret_cast<const bf16x8_t *>(tile + row * ROW_BYTES + ((fc ^ swz(row)) << 4));
     } else {
         constexpr int PITCH = R * 2;
         const int grp = lane >> 4, j = lane & 15;
         const int col = mn + 16 * (grp & 1) + 4 * (j & 3);
-        const int k = kk * 16 + 8 * (grp >> 1) + (j >> 2);
+        const int k = q * 16 + 8 * (grp >> 1) + (j >> 2);
         const int k2 = k + 4;
         const unsigned char *p0 =
             tile + k * PITCH + (((col >> 3) ^ swz_mn(k)) << 4) + ((col & 7) << 1);
@@ -216,45 +265,38 @@ __device__ __forceinline__ bf16x8_t read_frag(const unsigned char *tile, int mn,
     }
 }
 
-// One step's MFMA operands of a wave: two 16-wide K halves, TM A and TN B
-// 32-index fragments each.
+// One half stage's MFMA operands of a wave: two 16-wide K slices, TM A and
+// TN B 32-index fragments each.
 template <int TM, int TN>
 struct Frags {
     bf16x8_t a[2][TM], b[2][TN];
 };
 
-template <bool AK, bool BKM, int BM, int BN, int TM, int TN, int WTM, int WTN>
-__device__ __forceinline__ void read_frags(Frags<TM, TN> &f, const unsigned char *As,
-                                           const unsigned char *Bs, int wm, int wn, int lane)
+// Fragment read number o of half `h` (A fragments of K slice 0, B
+// fragments of slice 0, then the same for slice 1).
+template <bool AK, bool BKM, int BM, int BN, int TM, int TN, int WTM, int WTN, int O>
+__device__ __forceinline__ void read_one(Frags<TM, TN> &f, const unsigned char *As,
+                                         const unsigned char *Bs, int h, int wm, int wn, int lane)
 {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            f.a[kk][i] = read_frag<AK, BM>(As, wm * WTM + i * 32, kk, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            f.b[kk][j] = read_frag<BKM, BN>(Bs, wn * WTN + j * 32, kk, lane);
-    }
+    constexpr int kk = O / (TM + TN), idx = O % (TM + TN);
+    if constexpr (idx < TM)
+        f.a[kk][idx] = read_frag<AK, BM>(As, wm * WTM + idx * 32, 2 * h + kk, lane);
+    else
+        f.b[kk][idx - TM] = read_frag<BKM, BN>(Bs, wn * WTN + (idx - TM) * 32, 2 * h + kk, lane);
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[TM][TN], const Frags<TM, TN> &f)
+// MFMA number q of a half (q = kk * TM * TN + i * TN + j).
+template <int TM, int TN, int Q>
+__device__ __forceinline__ void mfma_one(f32x16_t (&acc)[TM][TN], const Frags<TM, TN> &f)
 {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j],
-                                                                     acc[i][j], 0, 0, 0);
+    constexpr int kk = Q / (TM * TN), i = (Q / TN) % TM, j = Q % TN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool AK, bool BKM, bool ROWSQ>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
 __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
 {
-    using C = DmaCfg<BM, BN, WM, WN, STAGES>;
+    using C = DmaCfg<BM, BN, WM, WN>;
     using DA = OperandDma<AK, BM, WM * WN>;
     using DB = OperandDma<BKM, BN, WM * WN>;
     constexpr int NT = C::NT;
@@ -262,7 +304,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold 32x32 MFMA tiles");
     static_assert(!ROWSQ || (AK && BM <= NT), "row sums of squares: K-major A, one row per thread");
-    static_assert(DA::PER + DB::PER == C::LPW, "load count");
+    static_assert(DA::PER + DB::PER == C::LPS, "load count");
 
     __shared__ __align__(1024) unsigned char smem[C::SMEM];
 
@@ -276,6 +318,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
     const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
     const int z = static_cast<int>(blockIdx.y);
 
+    // stages of the concatenated K range, and this split's share
     const int64_t st1 = (g.seg[0].K + BK - 1) / BK;
     const int64_t st_total = st1 + (g.nseg > 1 ? (g.seg[1].K + BK - 1) / BK : 0);
     int64_t s_begin = static_cast<int64_t>(z) * g.steps_per_split;
@@ -285,50 +328,78 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
     if (s_end > st_total)
         s_end = st_total;
 
-    // per-segment load plans and buffer descriptors (a K-major operand spans
-    // its M or N rows, an MN-major one its K rows)
+    // per-segment load plans and byte ranges (a K-major operand spans its M
+    // or N rows, an MN-major one its K rows)
     DA da0, da1;
     DB db0, db1;
     da0.init(g.M, g.seg[0].lda, m0, wave, lane);
     db0.init(g.N, g.seg[0].ldb, n0, wave, lane);
-    const __amdgpu_buffer_rsrc_t ra0 =
-        operand_rsrc(g.seg[0].a, (AK ? g.M : g.seg[0].K) * g.seg[0].lda * 2);
-    const __amdgpu_buffer_rsrc_t rb0 =
-        operand_rsrc(g.seg[0].b, (BKM ? g.N : g.seg[0].K) * g.seg[0].ldb * 2);
-    __amdgpu_buffer_rsrc_t ra1 = ra0, rb1 = rb0;
+    const int na0 = range_bytes((AK ? g.M : g.seg[0].K) * g.seg[0].lda * 2);
+    const int nb0 = range_bytes((BKM ? g.N : g.seg[0].K) * g.seg[0].ldb * 2);
+    int na1 = na0, nb1 = nb0;
     if (g.nseg > 1) {
         da1.init(g.M, g.seg[1].lda, m0, wave, lane);
         db1.init(g.N, g.seg[1].ldb, n0, wave, lane);
-        ra1 = operand_rsrc(g.seg[1].a, (AK ? g.M : g.seg[1].K) * g.seg[1].lda * 2);
-        rb1 = operand_rsrc(g.seg[1].b, (BKM ? g.N : g.seg[1].K) * g.seg[1].ldb * 2);
+        na1 = range_bytes((AK ? g.M : g.seg[1].K) * g.seg[1].lda * 2);
+        nb1 = range_bytes((BKM ? g.N : g.seg[1].K) * g.seg[1].ldb * 2);
     } else {
         da1 = da0;
         db1 = db0;
     }
 
-    auto stage_ptr = [&](int64_t s) {
-        return smem + static_cast<int>((s - s_begin) % STAGES) * C::STAGE_BYTES;
+    auto slot = [&](int64_t s) {
+        return smem + static_cast<int>((s - s_begin) & 1) * C::STAGE_BYTES;
     };
-    auto issue = [&](int64_t s) {
-        unsigned char *st = stage_ptr(s);
-        if (s < st1) {
-            da0.issue(st, ra0, s * BK, g.seg[0].lda, wave);
-            db0.issue(st + C::A_BYTES, rb0, s * BK, g.seg[0].ldb, wave);
+
+    // Load group d of stage sd (A tile groups first).  Stages past the end
+    // of this split go through descriptors with an empty range: they fetch
+    // nothing and deposit zeros in a slot no later stage reads, so every
+    // stage has the same shape (no branches, the same vmcnt bookkeeping).
+    constexpr int GA = DA::PER / GROUP, NG = C::LPS / GROUP;
+    auto dma_group = [&](int64_t sd, int d) {
+        const bool live = sd < s_end;
+        const bool sg1 = sd >= st1;
+        const int64_t kd = (sg1 ? sd - st1 : sd) * BK;
+        const int64_t kseg = sg1 ? g.seg[1].K : g.seg[0].K;
+        const bool isa = d < GA;
+        const int i0 = (isa ? d : d - GA) * GROUP;  // first instruction of the group
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((lds_void *)(slot(sd) + (isa ? 0 : C::A_BYTES) +
+                                                     (wave * (isa ? DA::PER : DB::PER) + i0) *
+                                                         1024))));
+        uint32_t v[GROUP];
+        uint32_t soff;
+        __amdgpu_buffer_rsrc_t rs;
+        if (isa) {
+            rs = scalar_rsrc(sg1 ? g.seg[1].a : g.seg[0].a, live ? (sg1 ? na1 : na0) : 0);
+            const int64_t ld = sg1 ? g.seg[1].lda : g.seg[0].lda;
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j) {
+                const uint32_t off = sg1 ? da1.off[i0 + j] : da0.off[i0 + j];
+                if constexpr (AK) {
+                    const uint32_t kq = sg1 ? da1.kch[i0 + j] : da0.kch[i0 + j];
+                    v[j] = kd + kq < kseg ? off : OOB_OFFSET;
+                } else {
+                    v[j] = off + static_cast<uint32_t>(kd * ld * 2);
+                }
+            }
+            soff = AK ? static_cast<uint32_t>(kd * 2) : 0u;
         } else {
-            da1.issue(st, ra1, (s - st1) * BK, g.seg[1].lda, wave);
-            db1.issue(st + C::A_BYTES, rb1, (s - st1) * BK, g.seg[1].ldb, wave);
+            rs = scalar_rsrc(sg1 ? g.seg[1].b : g.seg[0].b, live ? (sg1 ? nb1 : nb0) : 0);
+            const int64_t ld = sg1 ? g.seg[1].ldb : g.seg[0].ldb;
+#pragma unroll
+            for (int j = 0; j < GROUP; ++j) {
+                const uint32_t off = sg1 ? db1.off[i0 + j] : db0.off[i0 + j];
+                if constexpr (BKM) {
+                    const uint32_t kq = sg1 ? db1.kch[i0 + j] : db0.kch[i0 + j];
+                    v[j] = kd + kq < kseg ? off : OOB_OFFSET;
+                } else {
+                    v[j] = off + static_cast<uint32_t>(kd * ld * 2);
+                }
+            }
+            soff = BKM ? static_cast<uint32_t>(kd * 2) : 0u;
         }
-    };
-    // Wait until this wave's loads of step t have landed, given that at most
-    // `later` further steps (and none past s_end - 1) have been issued.
-    auto wait_step = [&](int64_t t, int later) {
-        const int64_t pend = (s_end - 1 - t) < later ? (s_end - 1 - t) : later;
-        if (pend >= 2)
-            wait_vmcnt<2 * C::LPW>();
-        else if (pend == 1)
-            wait_vmcnt<C::LPW>();
-        else
-            wait_vmcnt<0>();
+        lds_dma16x4(rs, lds, v[0], v[1], v[2], v[3], soff);
     };
 
     f32x16_t acc[TM][TN];
@@ -339,11 +410,14 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.f;
-    float sq[4] = {0.f, 0.f, 0.f, 0.f};  // ROWSQ: the row of A owned by this thread
-    auto rowsq_step = [&](const unsigned char *As) {
+    // ROWSQ: sum of squares of the A row owned by this thread, from the
+    // staged tile (8 chunks of a 128-byte row; 16 consecutive rows of a read
+    // phase hit distinct banks)
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+    auto rowsq_stage = [&](const unsigned char *As) {
         if (tn == 0 && tid < BM) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < 8; ++c) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(As + tid * ROW_BYTES +
                                                                  ((c ^ swz(tid)) << 4));
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -358,48 +432,75 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
         }
     };
 
-    // prologue: STAGES-1 steps in flight, then step s_begin visible and read
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-        if (s_begin + p < s_end)
-            issue(s_begin + p);
-
-    Frags<TM, TN> fa, fb;
-    if (s_begin < s_end) {
-        wait_step(s_begin, STAGES - 2);
-        stage_barrier();
-        read_frags<AK, BKM, BM, BN, TM, TN, WTM, WTN>(fa, stage_ptr(s_begin),
-                                                      stage_ptr(s_begin) + C::A_BYTES, wm, wn,
-                                                      lane);
-    }
-    // step s: the fragments of s are in `cur`; make s + 1 visible, refill the
-    // ring, read s + 1 into `nxt`, run the MFMAs of s.
-    auto body = [&](int64_t s, Frags<TM, TN> &cur, Frags<TM, TN> &nxt) {
-        const bool more = s + 1 < s_end;
-        // the reads of `cur` were issued a whole MFMA phase ago: retire them
-        // here, so that no wait lands between the reads of `nxt` and the MFMAs
+    // One half stage: the MFMAs of `cur` from registers and, between them,
+    // the fragment reads of the next half into `nxt` and (half 1 only) the
+    // loads of stage D + 2.  The scheduling barriers pin that interleaving:
+    // left to itself the compiler clusters the LDS reads, which stalls the
+    // single wave of a SIMD on a full LDS queue while its matrix core idles.
+    constexpr int NMF = 2 * TM * TN;    // MFMAs per half
+    constexpr int NRD = 2 * (TM + TN);  // fragment reads per half
+    using FR = Frags<TM, TN>;
+    auto half = [&](auto h_c, int64_t D, FR &cur, FR &nxt) {
+        constexpr int H = decltype(h_c)::value;
+        constexpr int NGH = H == 1 ? NG : 0;  // load groups in this half
+        constexpr int NOPS = NRD + NGH;
+        // the reads of `cur` were issued during the previous half: retire
+        // them here, so that no wait lands inside the interleaved sequence
         wait_lgkm0();
-        if (more)
-            wait_step(s + 1, STAGES - 3);
-        stage_barrier();
-        if (s + STAGES - 1 < s_end)
-            issue(s + STAGES - 1);
-        if constexpr (ROWSQ)
-            rowsq_step(stage_ptr(s));
-        if (more)
-            read_frags<AK, BKM, BM, BN, TM, TN, WTM, WTN>(nxt, stage_ptr(s + 1),
-                                                          stage_ptr(s + 1) + C::A_BYTES, wm, wn,
-                                                          lane);
-        mfma_step<TM, TN>(acc, cur);
+        if constexpr (H == 1) {
+            // stage D + 1 has landed (it is the only one in flight); after
+            // the barrier it is visible and every wave holds all of stage
+            // D's fragments, so its slot takes stage D + 2
+            wait_vmcnt<0>();
+            stage_barrier();
+        } else if constexpr (ROWSQ) {
+            rowsq_stage(slot(D));
+        }
+        // half 0 reads half 1 of the same stage; half 1 reads half 0 of D + 1
+        const unsigned char *An = slot(H == 0 ? D : D + 1);
+        const unsigned char *Bn = An + C::A_BYTES;
+        static_for<NMF>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            mfma_one<TM, TN, q>(acc, cur);
+            static_for<(q + 1) * NOPS / NMF - q * NOPS / NMF>([&](auto oc) {
+                constexpr int o = q * NOPS / NMF + decltype(oc)::value;
+                // load groups spread evenly, from the first slot on (they
+                // have a deadline; the reads only feed the next half)
+                constexpr int grp = (o * NGH) % NOPS < NGH ? (o * NGH) / NOPS : -1;
+                constexpr int rd = o - (o * NGH + NOPS - 1) / NOPS;
+                if constexpr (NGH > 0 && grp >= 0)
+                    dma_group(D + 2, grp);
+                else
+                    read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, rd>(nxt, An, Bn, 1 - H, wm, wn,
+                                                                    lane);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
-    int64_t s = s_begin;
-    for (; s + 1 < s_end; s += 2) {
-        body(s, fa, fb);
-        body(s + 1, fb, fa);
+
+    FR fa, fb;  // half 0 and half 1 of a stage
+    if (s_begin < s_end) {
+        // prologue: stages s_begin and s_begin + 1 in flight, then s_begin
+        // visible and the fragments of its half 0 read
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int d = 0; d < NG; ++d)
+                dma_group(s_begin + p, d);
+        wait_vmcnt<C::LPS>();
+        stage_barrier();
+        static_for<NRD>([&](auto oc) {
+            read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, decltype(oc)::value>(
+                fa, slot(s_begin), slot(s_begin) + C::A_BYTES, 0, wm, wn, lane);
+        });
+        // the last stage still reads a (stale) next slot; nothing uses it
+        for (int64_t D = s_begin; D < s_end; ++D) {
+            half(std::integral_constant<int, 0>{}, D, fa, fb);
+            half(std::integral_constant<int, 1>{}, D, fb, fa);
+        }
+        wait_vmcnt<0>();  // the empty loads past the end have deposited their zeros
     }
-    if (s < s_end)
-        body(s, fa, fb);
-    stage_barrier();  // every wave is done reading the stages before LDS is reused
+    stage_barrier();  // every wave is done reading the slots before LDS is reused
 
     if constexpr (ROWSQ) {
         if (g.rowsq != nullptr && tn == 0 && tid < BM && m0 + tid < g.M)
