@@ -64,6 +64,8 @@ struct GemmShape {
     int nseg;
     int layout;   // 0: A, B K-major; 1: B MN-major; 2: both MN-major
     bool dma_ok;  // direct-to-LDS kernel allowed (K-major K % 8, operands < 2 GiB)
+    bool rowdot = false;  // EPI_ROWDOT epilogue (else EPI_STORE)
+    bool rowsq = false;   // row sums of squares of A wanted
 };
 
 // Byte offsets of the direct-to-LDS kernel are 32-bit and carry a bias of
@@ -105,7 +107,7 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
         float rel;
         if (bf16) {
             const TileCfg t = gemm_bf16_cfg(c);
-            if (t.dma && !sh.dma_ok)
+            if ((t.dma && !sh.dma_ok) || (!t.store_ok && !sh.rowdot) || (sh.rowsq && !t.rowsq_ok))
                 continue;
             BM = t.BM;
             BN = t.BN;
@@ -168,10 +170,12 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, Carve &cv)
     const bool bf = dtype == DORA_BF16;
     NormPlan p;
     p.g = plan_gemm(bf, nt_shape(r, r, d_in), r * r);
-    p.u = plan_gemm(bf, nt_shape(d_out, r, d_in), 2 * d_out);
-    p.bg = plan_gemm(bf, GemmShape{d_out, r, {r, r}, bf ? 2 : 1, 1,
-                                   dma_operand(d_out, r) && dma_mn_operand(r, r)},
-                     d_out);
+    GemmShape us = nt_shape(d_out, r, d_in);
+    us.rowdot = us.rowsq = true;
+    p.u = plan_gemm(bf, us, 2 * d_out);
+    GemmShape bgs{d_out, r, {r, r}, bf ? 2 : 1, 1, dma_operand(d_out, r) && dma_mn_operand(r, r)};
+    bgs.rowdot = true;
+    p.bg = plan_gemm(bf, bgs, d_out);
     const size_t start = cv.off;
     p.o_gpart = cv.take(static_cast<size_t>(p.g.splits) * r * r * 4);
     p.o_gfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);

@@ -70,6 +70,8 @@ struct TileCfg {
     int bk;           // K values per step
     bool dma;         // pipelined direct-to-LDS kernel
     float rel_speed;  // relative throughput of a full tile, for planning
+    bool store_ok;    // EPI_STORE supported (else EPI_ROWDOT only)
+    bool rowsq_ok;    // row sums of squares of A supported
 };
 int gemm_bf16_num_cfgs();
 TileCfg gemm_bf16_cfg(int cfg);

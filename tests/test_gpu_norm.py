@@ -55,6 +55,29 @@ def test_norm_full_size_sampled_rows(shape):
     check_norm(np64(n)[rows], ref["n"], torch.bfloat16, f"{shape.name} sampled rows")
 
 
+@pytest.mark.parametrize("d_out,d_in,r", [
+    (12000, 2056, 384),   # whole-rank row-block tiles: ragged last block, K tail of 8
+    (40000, 1032, 200),   # rank below the tile width (ragged columns), K tail of 8
+])
+def test_norm_row_block_tiles(d_out, d_in, r):
+    """Shapes large enough that the planner takes the 128 x 384 row-block
+    tiles of the W A^T product (row sums and row dots formed from registers),
+    with ragged rows, columns and K; rows sampled, the last tile included."""
+    say("norm row-block tiles", d_out, d_in, r)
+    mod = synth.custom(d_out, d_in, r, 1, "bf16", 1.0, sigma_B=0.05, seed=r)
+    W, A, B = mod["W"], mod["A"], mod["B"]
+    out = D.dora_factored_norm(gpu(W), gpu(A), gpu(B), 1.0, terms=True)
+    torch.cuda.synchronize()
+    rows = sorted(set(sample_ids(3, 40, d_out) + list(range(d_out - 130, d_out))))
+    ref = O.norm(W, A, B, 1.0, rows=rows)
+    got = {k: np64(v)[rows] for k, v in zip(("n", "base", "cross", "gram"), out)}
+    check_norm(got["n"], ref["n"], torch.bfloat16, f"norm {d_out}x{d_in} r{r}")
+    scale = ref["n"] ** 2 + ref["base"]
+    for name in ("base", "cross", "gram"):
+        err = np.abs(got[name] - ref[name]) / scale
+        assert err.max() <= 2e-4, f"{name}: max err {err.max():.2e} of n^2 scale"
+
+
 def test_norm_near_cancellation():
     """Rows with W_i close to -s B_i A: ||W_i + s B_i A|| is 0.1 or 0.01 of
     ||W_i||.  The factored sum subtracts nearly equal terms there; the error
