@@ -71,6 +71,7 @@ struct GemmShape {
 // Byte offsets of the direct-to-LDS kernel are 32-bit and carry a bias of
 // up to 3 KiB (grouped loads); keep every operand's range below 2 GiB - 4 KiB.
 constexpr int64_t kDmaBytes = (1LL << 31) - 4096;
+constexpr double kWaveOverhead = 8e-6;  // seconds per wave of workgroups
 
 // Operands the direct-to-LDS kernel can take (bf16, byte offsets < 2 GiB):
 // a K-major one of `rows` x `K` loads whole 16-byte chunks (K % 8) and zeros
@@ -129,8 +130,12 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
                 break;
             const int64_t sps = (steps + z - 1) / z;
             const int64_t waves = std::max<int64_t>((tiles * z + kCUs - 1) / kCUs, 1);
-            double cost = static_cast<double>(waves) * 2.0 * BM * BN * bk *
-                          static_cast<double>(std::max<int64_t>(sps, 1)) / (cu_flops * rel);
+            // a wave of workgroups also pays its pipeline fill and epilogue
+            // (measured: about 8 us on the row-dot products of the norm)
+            double cost = static_cast<double>(waves) *
+                          (2.0 * BM * BN * bk * static_cast<double>(std::max<int64_t>(sps, 1)) /
+                               (cu_flops * rel) +
+                           kWaveOverhead);
             if (z > 1)
                 cost += 2.0 * z * part_per_split * 4.0 / hbm + 3e-6;
             if (best_cost < 0 || cost < best_cost * 0.97) {

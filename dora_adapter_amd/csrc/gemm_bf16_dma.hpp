@@ -503,7 +503,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
 #pragma unroll
             for (int d = 0; d < NG; ++d)
                 dma_group(s_begin + p, d);
-        wait_vmcnt<C::LPS>();
+        wait_vmcnt<C::LPS>();  // stage s_begin has landed
         stage_barrier();
         static_for<NRD>([&](auto oc) {
             read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, decltype(oc)::value>(

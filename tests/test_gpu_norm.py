@@ -58,16 +58,22 @@ def test_norm_full_size_sampled_rows(shape):
 @pytest.mark.parametrize("d_out,d_in,r", [
     (12000, 2056, 384),   # whole-rank row-block tiles: ragged last block, K tail of 8
     (40000, 1032, 200),   # rank below the tile width (ragged columns), K tail of 8
+    (5120, 27648, 384),   # few row blocks, long K: split over K
 ])
 def test_norm_row_block_tiles(d_out, d_in, r):
     """Shapes large enough that the planner takes the 128 x 384 row-block
     tiles of the W A^T product (row sums and row dots formed from registers),
-    with ragged rows, columns and K; rows sampled, the last tile included."""
+    with ragged rows, columns and K, and split K; rows sampled, the last tile
+    included; a second call must agree bit for bit."""
     say("norm row-block tiles", d_out, d_in, r)
     mod = synth.custom(d_out, d_in, r, 1, "bf16", 1.0, sigma_B=0.05, seed=r)
-    W, A, B = mod["W"], mod["A"], mod["B"]
-    out = D.dora_factored_norm(gpu(W), gpu(A), gpu(B), 1.0, terms=True)
+    W, A, B = gpu(mod["W"]), gpu(mod["A"]), gpu(mod["B"])
+    out = D.dora_factored_norm(W, A, B, 1.0, terms=True)
+    again = D.dora_factored_norm(W, A, B, 1.0, terms=True)
     torch.cuda.synchronize()
+    for a, b in zip(out, again):
+        assert torch.equal(a, b), "factored norm not deterministic"
+    W, A, B = mod["W"], mod["A"], mod["B"]
     rows = sorted(set(sample_ids(3, 40, d_out) + list(range(d_out - 130, d_out))))
     ref = O.norm(W, A, B, 1.0, rows=rows)
     got = {k: np64(v)[rows] for k, v in zip(("n", "base", "cross", "gram"), out)}
