@@ -214,6 +214,52 @@ int oracle_compose(const void *base, const void *lora, const double *m,
 }
 
 /*
+ * Merged weight, by its plain definition: W'[q, j] = (m_i / n_i) * V[i, j]
+ * for the listed rows i = rows[q] (rows == NULL: all d_out rows), with
+ * V = W + s*B*A and n_i its dense row norm, or n_in[i] when given.  The
+ * adapted weight folds into one matrix, so inference runs a plain linear
+ * layer ([DoRA] Key Points 3 and 5: no added inference latency).  Wm is
+ * [nrows][d_in] double.
+ */
+int oracle_merge(const void *W, const void *A, const void *B, const double *m,
+                 int dt, double s, int64_t d_out, int64_t d_in, int64_t r,
+                 const int64_t *rows, int64_t nrows, const double *n_in, double *Wm)
+{
+    if (rows == NULL)
+        nrows = d_out;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *ba = malloc(sizeof(double) * (size_t)(d_in > 0 ? d_in : 1));
+        double *v = malloc(sizeof(double) * (size_t)(d_in > 0 ? d_in : 1));
+        if (ba == NULL || v == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t q = 0; q < nrows; ++q) {
+                int64_t i = rows ? rows[q] : q;
+                dense_row(W, A, B, dt, s, d_in, r, i, ba, v);
+                double ni = 0.0;
+                if (n_in) {
+                    ni = n_in[i];
+                } else {
+                    for (int64_t j = 0; j < d_in; ++j)
+                        ni += v[j] * v[j];
+                    ni = sqrt(ni);
+                }
+                for (int64_t j = 0; j < d_in; ++j)
+                    Wm[q * d_in + j] = (m[i] / ni) * v[j];
+            }
+        }
+        free(ba);
+        free(v);
+    }
+    (void)d_out;
+    return failed ? -1 : 0;
+}
+
+/*
  * Backward with the row norm n held constant, all outputs, for sizes the
  * dense [d_out, d_in] V fits in host memory.  With g_i = m_i / n_i,
  * h = x V^T and dh = dy (.) g:

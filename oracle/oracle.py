@@ -52,7 +52,9 @@ def _declare(lib):
                                             _d, _i64, _i64, _i64, _i64,
                                             _p, _i64, _p, _p, _i64, _p,
                                             _p, _i64, _p, _p, _i64, _p]
-    for f in ("oracle_norm", "oracle_forward", "oracle_compose",
+    lib.oracle_merge.argtypes = [_p, _p, _p, _p, ctypes.c_int, _d, _i64, _i64, _i64,
+                                 _p, _i64, _p, _p]
+    for f in ("oracle_norm", "oracle_forward", "oracle_compose", "oracle_merge",
               "oracle_backward_full", "oracle_backward_sampled"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
@@ -168,6 +170,25 @@ def compose(base, lora, m, n, s):
     load().oracle_compose(_ptr(bb), _ptr(ll), _ptr(_f64(m)), _ptr(_f64(n)), dt, _s(s),
                           T, d_out, _ptr(y))
     return y
+
+
+def merge(W, A, B, m, s, rows=None, n_in=None):
+    """Merged weight W'[i] = (m_i/n_i) (W + s B A)[i] for the listed rows
+    (all by default), [nrow, d_in] float64; n from the dense rows unless
+    n_in is given."""
+    (w, dw), (a, da), (b, db) = _raw(W), _raw(A), _raw(B)
+    dt = _same_dtype(dw, da, db)
+    d_out, d_in = w.shape
+    r = a.shape[0]
+    rw = _idx(rows)
+    nr = d_out if rw is None else rw.size
+    nin = None if n_in is None else _f64(n_in)
+    out = np.zeros((nr, d_in))
+    rc = load().oracle_merge(_ptr(w), _ptr(a), _ptr(b), _ptr(_f64(m)), dt, _s(s), d_out, d_in,
+                             r, _ptr(rw), nr, _ptr(nin), _ptr(out))
+    if rc:
+        raise MemoryError("oracle_merge failed")
+    return out
 
 
 def backward_full(dy, x, W, A, B, m, n, s):

@@ -328,8 +328,36 @@ def pin_compose_reductions():
     _close(yc, yf, 1e-15, 1e-15, "compose vs forward")
 
 
+def pin_hand_merge():
+    g = load_golden()
+    W, A, B = _t32(g["W"]), _t32(g["A"]), _t32(g["B"])
+    for s, key in ((2.0, "s2"), (0.5, "s05")):
+        _close(O.merge(W, A, B, g["m"], s), g[f"{key}.merge"], 1e-15, 1e-15, f"hand {key}.merge")
+
+
+def pin_merge_properties():
+    """The merged rows have norm m_i and the direction of V_i = W_i + s B_i A
+    (V along numpy's route); x W'^T reproduces the oracle forward; rows and
+    a given n select and fix as in the forward."""
+    for dtype in (torch.float32, torch.bfloat16):
+        W, A, B, m, x, _ = _rand_module(16, 19, 27, 4, 6, dtype)
+        s = 1.25
+        Wm = O.merge(W, A, B, m, s)
+        _close(np.linalg.norm(Wm, axis=1), _np64(m), 1e-14, 0, "merged row norms = m")
+        V = _np64(W) + s * _np64(B) @ _np64(A)
+        unit = V / np.linalg.norm(V, axis=1, keepdims=True)
+        _close(Wm / np.linalg.norm(Wm, axis=1, keepdims=True), unit, 1e-13, 1e-15,
+               "merged direction")
+        y, _ = O.forward(x, W, A, B, m, s)
+        _close(_np64(x) @ Wm.T, y, 1e-12, 1e-13, "x W'^T = forward")
+        rows = [18, 0, 7]
+        assert np.array_equal(O.merge(W, A, B, m, s, rows=rows), Wm[rows]), "merge rows"
+        n = O.norm(W, A, B, s)["n"]
+        assert np.array_equal(O.merge(W, A, B, m, s, n_in=2 * n), Wm / 2), "merge with n_in"
+
+
 ALL_PINS = [pin_hand_norm, pin_hand_forward, pin_hand_backward, pin_factored_identity,
             pin_textbook_b0, pin_rank1, pin_orthogonal, pin_forward_b0_exact,
             pin_forward_lora_reduction, pin_forward_scale_invariance, pin_forward_linearity,
             pin_forward_subsets, pin_backward_autograd, pin_backward_finite_differences,
-            pin_compose_reductions]
+            pin_compose_reductions, pin_hand_merge, pin_merge_properties]

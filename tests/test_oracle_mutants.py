@@ -39,6 +39,11 @@ MUTANTS = {
     "sampled_dx_no_g": ("acc += elem(dy, dt, t * d_out + i) * (m[i] / n[i]) * vij;",
                         "acc += elem(dy, dt, t * d_out + i) * vij;"),
     "sampled_dm_over_m": ("dm[q] = acc / n[i];", "dm[q] = acc / m[i];"),
+    "merge_g_inverted": ("Wm[q * d_in + j] = (m[i] / ni) * v[j];",
+                         "Wm[q * d_in + j] = (ni / m[i]) * v[j];"),
+    "merge_base_only": ("Wm[q * d_in + j] = (m[i] / ni) * v[j];",
+                        "Wm[q * d_in + j] = (m[i] / ni) * elem(W, dt, i * d_in + j);"),
+    "merge_norm_squared": ("ni = sqrt(ni);", "ni = ni;"),
 }
 
 
