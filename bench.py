@@ -18,6 +18,8 @@ Printed JSON line (one):
                the 2.5 PFLOP/s dense bf16 MFMA peak.
   roofline     the dominant kernel (the base product x W^T, bf16 MFMA),
                timed with HIP events on the launch stream.
+  merge_*      dora_merge alone (norm given): the merged inference weight,
+               HBM GB/s (read W, write W').
   cpu_baseline the fp64 oracle forward on the same module on the host cores,
                on a bounded token sample, extrapolated to the full batch.
 """
@@ -222,6 +224,18 @@ def main():
         out["norm_us"] = round(norm_us, 1)
         out["norm_mfma_util"] = round(nf / norm_us / 1e6 / PEAK_BF16_TFLOPS, 4)
         log(f"norm {norm_us:.1f} us = {nf / norm_us / 1e6:.0f} TFLOP/s")
+
+        # merged weight for inference (norm given): read W, write W', 2 x 2 bytes per weight
+        w_out = torch.empty_like(t["W"])
+        ws_m = torch.empty(D.dora_merge_workspace(d_out, d_in, r, 1), dtype=torch.uint8,
+                           device=dev)
+        merge_us = timed(lambda: D.dora_merge(t["W"], t["A"], t["B"], t["m"], s, n_in=n2,
+                                              out=w_out, ws=ws_m))
+        merge_bytes = 2 * d_out * d_in * 2 + (d_out + d_in) * r * 2 + 2 * d_out * 4
+        out["merge_us"] = round(merge_us, 1)
+        out["merge_GBps"] = round(merge_bytes / merge_us / 1e3, 1)
+        log(f"merge {merge_us:.1f} us = {merge_bytes / merge_us / 1e3:.0f} GB/s")
+        del w_out, ws_m
 
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         lora = torch.randn(T, d_out, device=dev).bfloat16()

@@ -210,6 +210,32 @@ LinPlan plan_linear(int64_t T, int64_t d_in, int64_t d_out, int dtype)
     return l;
 }
 
+// Merge: the norm (unless the caller has it) and one product C = B A (M =
+// d_out, N = d_in, K = r) whose epilogue forms W' = W + ((g - 1) W + g s C)
+// by rows.  The epilogue needs whole sums, so the product is never split.
+constexpr int64_t kNoSplit = int64_t(1) << 40;  // part_per_split that rules out split-K
+
+struct MergePlan {
+    NormPlan norm;
+    GPlan g;
+    size_t o_n;
+    size_t bytes;
+};
+
+MergePlan plan_merge(int64_t d_out, int64_t d_in, int64_t r, int dtype)
+{
+    const bool bf = dtype == DORA_BF16;
+    MergePlan p;
+    Carve cv;
+    p.norm = plan_norm(d_out, d_in, r, dtype, cv);
+    p.o_n = cv.take(static_cast<size_t>(d_out) * 4);
+    const GemmShape sh{d_out, d_in, {r, 0}, 1, 1,
+                       dma_operand(d_out, r) && dma_mn_operand(r, d_in)};
+    p.g = plan_gemm(bf, sh, kNoSplit);
+    p.bytes = cv.off;
+    return p;
+}
+
 // Forward: the norm, P = x A^T, then one K-concatenated product
 // [x | s P] [W | B]^T whose fp32 accumulator h = x W^T + s P B^T is stored as
 // (m/n) h by the epilogue (no [T, d_out] intermediate).
@@ -698,6 +724,57 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
     // 5. dA = Q^T x  (both MN-major, K = T).
     DORA_CHECK(run_store(bf, p.dA, seg1(r, d_in, Q, r, x, d_in, T), 2, dA, d_in, 1.0f,
                          reinterpret_cast<float *>(w + p.o_dApart), st, "dA"));
+    return DORA_OK;
+}
+
+size_t dora_merge_workspace(int64_t d_out, int64_t d_in, int64_t r, int dtype)
+{
+    if (check_dtype(dtype) || check_dims(dtype, 0, d_in, d_out, r))
+        return 0;
+    return plan_merge(d_out, d_in, r, dtype).bytes;
+}
+
+int dora_merge(const void *W, const void *A, const void *B, const float *m, float s,
+               int64_t d_out, int64_t d_in, int64_t r, int dtype, const float *n_in, void *W_out,
+               void *ws, size_t ws_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_dims(dtype, 0, d_in, d_out, r));
+    DORA_CHECK(check_ptrs({{W, "W", true}, {A, "A", true}, {B, "B", true}, {m, "m", true},
+                           {W_out, "W_out", true}, {n_in, "n_in", false}}));
+    const MergePlan p = plan_merge(d_out, d_in, r, dtype);
+    DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
+    const bool bf = dtype == DORA_BF16;
+    const size_t e = esize(dtype);
+    const Range rW{W, d_out * d_in * e}, rA{A, r * d_in * e}, rB{B, d_out * r * e},
+        rm{m, d_out * sizeof(float)}, rnin{n_in, d_out * sizeof(float)};
+    const Range rout{W_out, d_out * d_in * e}, rws{ws, p.bytes};
+    if (W_out != W && overlap(rout, rW))
+        return fail(DORA_E_ALIAS, "W_out partially overlaps W");
+    DORA_CHECK(check_disjoint({{rout, "W_out"}, {rws, "workspace"}},
+                              {{rA, "A"}, {rB, "B"}, {rm, "m"}, {rnin, "n_in"}}));
+    DORA_CHECK(check_disjoint({{rws, "workspace"}}, {{rW, "W"}, {rout, "W_out"}}));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    const float *n = n_in;
+    if (n == nullptr) {
+        float *nw = reinterpret_cast<float *>(w + p.o_n);
+        DORA_CHECK(norm_impl(W, A, B, s, d_out, d_in, r, dtype, nw, nullptr, nullptr, nullptr,
+                             p.norm, w, st));
+        n = nw;
+    }
+    GemmArgs g = seg1(d_out, d_in, B, r, A, d_in, r);
+    g.mode = EPI_MERGE;
+    g.E = W;
+    g.lde = d_in;
+    g.colm = m;
+    g.coln = n;
+    g.alpha = s;
+    g.out = W_out;
+    g.ldc = d_in;
+    DORA_LAUNCH(run_gemm(bf, p.g, g, 1, false, st), "merge W + s B A");
     return DORA_OK;
 }
 

@@ -26,6 +26,9 @@ struct GemmSeg {
 enum EpiMode : int {
     EPI_STORE = 0,   // out[m, n] = alpha * C (dtype of the kernel or fp32), split z at out + z*M*ldc
     EPI_ROWDOT = 1,  // rowdot[(z*ntn + tn)*M + m] = sum_{n in tile} C[m, n] * E[m, n]
+    // out[m, n] = E[m, n] + ((g_m - 1) E[m, n] + g_m alpha C[m, n]), g_m =
+    // colm[m] / coln[m] (row factors here), rounded once; one split only
+    EPI_MERGE = 2,
 };
 
 struct GemmArgs {
@@ -42,10 +45,11 @@ struct GemmArgs {
     float alpha;
     // optional per-column magnitude scale of the store: with colm and coln
     // set, column n of alpha * C is stored as h + ((colm[n] - coln[n]) /
-    // coln[n]) h, i.e. (m/n) h in the cancellation-safe form
+    // coln[n]) h, i.e. (m/n) h in the cancellation-safe form (EPI_MERGE:
+    // per-row factors)
     const float *colm;
     const float *coln;
-    // EPI_ROWDOT
+    // EPI_ROWDOT, EPI_MERGE
     const void *E;
     int64_t lde;
     float *rowdot;

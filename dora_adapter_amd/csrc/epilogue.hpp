@@ -153,6 +153,55 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
                     o[q] = v[q];
             }
         }
+    } else if (g.mode == EPI_MERGE) {
+        // W' = W + ((g - 1) W + g s C) by rows, g = m / n, rounded once; all
+        // operands of the thread's chunks are loaded before any is stored
+        // (W' may be W itself: each element is read, then written, by the
+        // same thread)
+        const TE *E = static_cast<const TE *>(g.E);
+        EChunk<TE> e[ITER];
+        float gm1[ITER], gs[ITER];
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int64_t m = mrow0 + row0 + it * RSTEP;
+            const bool live = m < M && cnt > 0;
+            if (live)
+                e[it].load(E + m * g.lde + n, cnt);
+            else
+                e[it].zero();
+            const float mi = live ? g.colm[m] : 1.f;
+            const float ni = live ? g.coln[m] : 1.f;
+            gm1[it] = (mi - ni) / ni;
+            gs[it] = (mi / ni) * g.alpha;
+        }
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int row = row0 + it * RSTEP;
+            const int64_t m = mrow0 + row;
+            if (m >= M || cnt == 0)
+                continue;
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float w = e[it].get(q);
+                v[q] = w + __fmaf_rn(gm1[it], w, gs[it] * Cs[row * CST + c * 8 + q]);
+            }
+            if constexpr (sizeof(TE) == 2) {
+                uint16_t *o = static_cast<uint16_t *>(g.out) + m * g.ldc + n;
+                if (cnt == 8) {
+                    *reinterpret_cast<uint4 *>(o) =
+                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+                } else {
+                    for (int q = 0; q < cnt; ++q)
+                        o[q] = f32_to_bf16(v[q]);
+                }
+            } else {
+                float *o = static_cast<float *>(g.out) + m * g.ldc + n;
+                for (int q = 0; q < cnt; ++q)
+                    o[q] = v[q];
+            }
+        }
     } else {  // EPI_ROWDOT
         const int ntn = static_cast<int>((N + BN - 1) / BN);
         const TE *E = static_cast<const TE *>(g.E);

@@ -413,7 +413,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
 {
     if (rowsq && layout != 0)
         return hipErrorInvalidValue;
-    if (cfg < 0 || cfg >= gemm_bf16_num_cfgs() || (a.mode == EPI_STORE && !kCfgs[cfg].store_ok) ||
+    if (cfg < 0 || cfg >= gemm_bf16_num_cfgs() || (a.mode != EPI_ROWDOT && !kCfgs[cfg].store_ok) ||
         (rowsq && !kCfgs[cfg].rowsq_ok))
         return hipErrorInvalidValue;
     switch (cfg) {

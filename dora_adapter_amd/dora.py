@@ -21,7 +21,8 @@ STATUS = {0: "DORA_OK", 1: "DORA_E_NULL", 2: "DORA_E_SHAPE", 3: "DORA_E_DTYPE",
 # Every symbol include/dora.h declares.
 EXPORTS = ("dora_strerror", "dora_last_error", "dora_norm_workspace", "dora_forward_workspace",
            "dora_backward_workspace", "dora_factored_norm", "dora_compose", "dora_forward",
-           "dora_backward", "dora_linear_workspace", "dora_linear")
+           "dora_backward", "dora_linear_workspace", "dora_linear", "dora_merge_workspace",
+           "dora_merge")
 
 _lib = None
 
@@ -65,6 +66,10 @@ def lib():
         L.dora_linear_workspace.argtypes = [i64, i64, i64, c_int]
         L.dora_linear.restype = c_int
         L.dora_linear.argtypes = [p, p, i64, i64, i64, c_int, p, p, sz, p]
+        L.dora_merge_workspace.restype = sz
+        L.dora_merge_workspace.argtypes = [i64, i64, i64, c_int]
+        L.dora_merge.restype = c_int
+        L.dora_merge.argtypes = [p, p, p, p, f, i64, i64, i64, c_int, p, p, p, sz, p]
         _lib = L
     return _lib
 
@@ -198,3 +203,22 @@ def dora_linear(x, W, y=None, ws=None):
     _check(lib().dora_linear(_ptr(x), _ptr(W), T, d_in, d_out, dt, _ptr(y), _ptr(ws),
                              0 if ws is None else ws.numel(), _stream(dev)))
     return y
+
+
+def dora_merge_workspace(d_out, d_in, r, dtype):
+    return lib().dora_merge_workspace(d_out, d_in, r, dtype)
+
+
+def dora_merge(W, A, B, m, s, n_in=None, out=None, ws=None):
+    """Merged weight W' = (m/n) (W + s B A) by rows (n factored unless n_in
+    is given); out may be W itself."""
+    dev = _dev(W)
+    d_out, d_in = W.shape
+    r = A.shape[0]
+    dt = _dt(W)
+    out = torch.empty_like(W) if out is None else out
+    need = lib().dora_merge_workspace(d_out, d_in, r, dt)
+    ws = _ws(need, dev) if ws is None else ws
+    _check(lib().dora_merge(_ptr(W), _ptr(A), _ptr(B), _ptr(m), float(s), d_out, d_in, r, dt,
+                            _ptr(n_in), _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out

@@ -176,6 +176,25 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
                   void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * dora_merge - the merged weight W' = g (.) (W + s B A), g = m / n by rows,
+ * for inference: the DoRA summary pages ("Method"; Key Points 3 and 5) note
+ * that the adapted weight folds into the base weight, so inference is a
+ * plain linear layer (dora_linear).  n is the factored row norm of the
+ * "Scaling DoRA" abstract (computed here unless n_in is given), so no dense
+ * B A product is kept: B A is formed tile by tile inside one product whose
+ * epilogue writes W'[i, j] = W[i, j] + ((g_i - 1) W[i, j] + g_i s (BA)[i, j])
+ * in fp32, rounded once (the near-unity form of dora_compose).
+ *   W, W_out [d_out, d_in], A [r, d_in], B [d_out, r] in `dtype`; m and
+ *   n_in (nullable) [d_out] fp32.  W_out may be W itself (in place) but must
+ *   not overlap it otherwise, nor A, B, m, n_in or the workspace.
+ *   ws: dora_merge_workspace(d_out, d_in, r, dtype) bytes.
+ */
+size_t dora_merge_workspace(int64_t d_out, int64_t d_in, int64_t r, int dtype);
+int dora_merge(const void *W, const void *A, const void *B, const float *m, float s,
+               int64_t d_out, int64_t d_in, int64_t r, int dtype, const float *n_in, void *W_out,
+               void *ws, size_t ws_bytes, void *stream);
+
+/*
  * dora_linear - y = x W^T on the same kernel and launch plan dora_forward
  * uses for its base term.  With W = W' = g (.) (W + sBA), the weight merged
  * after training, this is the whole DoRA inference path: the DoRA summary

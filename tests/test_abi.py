@@ -180,3 +180,35 @@ def test_backward_validation():
     assert call(dx=base[0]) == E_ALIAS                  # dx over dy
     assert call(dB=base[10] + 64) == E_ALIAS            # dB inside dA
     assert call(T=-1) == E_SHAPE
+
+
+def _merge(W=FAKE, A=FAKE + (1 << 32), B=FAKE + (2 << 32), m=FAKE + (3 << 32), n_in=0,
+           out=FAKE + (4 << 32), d_out=64, d_in=128, r=8, dt=BF16, ws=FAKE + (5 << 32),
+           ws_bytes=None):
+    L = D.lib()
+    if ws_bytes is None:
+        ws_bytes = max(L.dora_merge_workspace(d_out, d_in, r, BF16), 1)
+    return L.dora_merge(_p(W), _p(A), _p(B), _p(m), 1.0, d_out, d_in, r, dt, _p(n_in), _p(out),
+                        _p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"W": 0}, E_NULL), ({"out": 0}, E_NULL), ({"m": 0}, E_NULL), ({"dt": 3}, E_DTYPE),
+    ({"r": 0}, E_SHAPE), ({"d_in": 100}, E_SHAPE), ({"A": FAKE + (1 << 32) + 8}, E_ALIGN),
+    ({"ws": 0}, E_WS), ({"ws_bytes": 8}, E_WS),
+    ({"out": FAKE + 256}, E_ALIAS),                   # W_out partially overlaps W
+    ({"out": FAKE + (2 << 32)}, E_ALIAS),             # W_out over B
+    ({"ws": FAKE + 4096}, E_ALIAS),                   # workspace inside W
+])
+def test_merge_validation(kw, code):
+    assert _merge(**kw) == code
+    assert D.lib().dora_last_error()
+
+
+def test_merge_workspace_has_no_dense_term():
+    """The merge keeps no [d_out, d_in] buffer besides its output: its
+    workspace is the norm's plus one fp32 vector of row norms."""
+    L = D.lib()
+    for d_out, d_in in ((8192, 8192), (28672, 8192), (8192, 262144)):
+        ws = L.dora_merge_workspace(d_out, d_in, 384, BF16)
+        assert 0 < ws <= L.dora_norm_workspace(d_out, d_in, 384, BF16) + d_out * 4 + 256
