@@ -260,6 +260,127 @@ int oracle_merge(const void *W, const void *A, const void *B, const double *m,
 }
 
 /*
+ * Backward through the row norm (the gradient without the stop-gradient),
+ * all outputs, by the plain chain rule on dense V = W + s*B*A.  Here n is
+ * the dense row norm of V itself.  With h = x V^T, g = m / n and
+ * dh = dy (.) g, the gradient with respect to V is
+ *   dV[i,j] = sum_t dh[t,i] x[t,j] - cn_i V[i,j],
+ *   cn_i    = (m_i / n_i^3) sum_t dy[t,i] h[t,i]      (from dn_i/dV_i = V_i / n_i),
+ * and, as V depends on A and B through s*B*A,
+ *   dA[k,j] = s * sum_i B[i,k] dV[i,j],   dB[i,k] = s * sum_j dV[i,j] A[k,j];
+ * dx and dm are the same as with n held constant (n depends on neither).
+ * Outputs are double: dx [T][d_in], dA [r][d_in], dB [d_out][r], dm [d_out].
+ */
+int oracle_backward_through_norm(const void *dy, const void *x, const void *W,
+                                 const void *A, const void *B, const double *m,
+                                 int dt, double s, int64_t T, int64_t d_in,
+                                 int64_t d_out, int64_t r, double *dx, double *dA,
+                                 double *dB, double *dm)
+{
+    size_t nv = (size_t)(d_out * d_in > 0 ? d_out * d_in : 1);
+    size_t nh = (size_t)(T * d_out > 0 ? T * d_out : 1);
+    size_t nr = (size_t)(d_out > 0 ? d_out : 1);
+    double *V = malloc(sizeof(double) * nv);
+    double *dV = malloc(sizeof(double) * nv);
+    double *hv = malloc(sizeof(double) * nh);
+    double *nn = malloc(sizeof(double) * nr);
+    double *cn = malloc(sizeof(double) * nr);
+    int rc = 0;
+    if (!V || !dV || !hv || !nn || !cn) {
+        rc = -1;
+        goto done;
+    }
+
+    /* Dense V and its row norms. */
+#pragma omp parallel
+    {
+        double *ba = malloc(sizeof(double) * (size_t)(d_in > 0 ? d_in : 1));
+        if (ba != NULL) {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t i = 0; i < d_out; ++i) {
+                dense_row(W, A, B, dt, s, d_in, r, i, ba, V + i * d_in);
+                double sq = 0.0;
+                for (int64_t j = 0; j < d_in; ++j)
+                    sq += V[i * d_in + j] * V[i * d_in + j];
+                nn[i] = sqrt(sq);
+            }
+        } else {
+#pragma omp atomic write
+            rc = -1;
+        }
+        free(ba);
+    }
+    if (rc)
+        goto done;
+
+    /* h = x V^T. */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < d_out; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < d_in; ++j)
+                acc += elem(x, dt, t * d_in + j) * V[i * d_in + j];
+            hv[t * d_out + i] = acc;
+        }
+
+    /* dm and the norm coefficient cn. */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < d_out; ++i) {
+        double dyh = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            dyh += elem(dy, dt, t * d_out + i) * hv[t * d_out + i];
+        dm[i] = dyh / nn[i];
+        cn[i] = m[i] / (nn[i] * nn[i] * nn[i]) * dyh;
+    }
+
+    /* dV. */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < d_out; ++i)
+        for (int64_t j = 0; j < d_in; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                acc += elem(dy, dt, t * d_out + i) * (m[i] / nn[i]) * elem(x, dt, t * d_in + j);
+            dV[i * d_in + j] = acc - cn[i] * V[i * d_in + j];
+        }
+
+    /* dx = dh V. */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < d_in; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < d_out; ++i)
+                acc += elem(dy, dt, t * d_out + i) * (m[i] / nn[i]) * V[i * d_in + j];
+            dx[t * d_in + j] = acc;
+        }
+
+    /* dA = s B^T dV, dB = s dV A^T. */
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < r; ++k)
+        for (int64_t j = 0; j < d_in; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < d_out; ++i)
+                acc += elem(B, dt, i * r + k) * dV[i * d_in + j];
+            dA[k * d_in + j] = acc * s;
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < d_out; ++i)
+        for (int64_t k = 0; k < r; ++k) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < d_in; ++j)
+                acc += dV[i * d_in + j] * elem(A, dt, k * d_in + j);
+            dB[i * r + k] = acc * s;
+        }
+
+done:
+    free(V);
+    free(dV);
+    free(hv);
+    free(nn);
+    free(cn);
+    return rc;
+}
+
+/*
  * Backward with the row norm n held constant, all outputs, for sizes the
  * dense [d_out, d_in] V fits in host memory.  With g_i = m_i / n_i,
  * h = x V^T and dh = dy (.) g:

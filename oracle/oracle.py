@@ -54,8 +54,11 @@ def _declare(lib):
                                             _p, _i64, _p, _p, _i64, _p]
     lib.oracle_merge.argtypes = [_p, _p, _p, _p, ctypes.c_int, _d, _i64, _i64, _i64,
                                  _p, _i64, _p, _p]
+    lib.oracle_backward_through_norm.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _d,
+                                                 _i64, _i64, _i64, _i64, _p, _p, _p, _p]
     for f in ("oracle_norm", "oracle_forward", "oracle_compose", "oracle_merge",
-              "oracle_backward_full", "oracle_backward_sampled"):
+              "oracle_backward_full", "oracle_backward_sampled",
+              "oracle_backward_through_norm"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -206,6 +209,25 @@ def backward_full(dy, x, W, A, B, m, n, s):
                                      _ptr(out["dB"]), _ptr(out["dm"]))
     if rc:
         raise MemoryError("oracle_backward_full failed")
+    return out
+
+
+def backward_through_norm(dy, x, W, A, B, m, s):
+    """All gradients with the gradient flowing through n (no stop-gradient);
+    n is the dense row norm.  Dict of float64 arrays."""
+    (g, d0), (xx, d1), (w, d2), (a, d3), (b, d4) = (_raw(dy), _raw(x), _raw(W), _raw(A),
+                                                    _raw(B))
+    dt = _same_dtype(d0, d1, d2, d3, d4)
+    T, d_in = xx.shape
+    d_out, r = w.shape[0], a.shape[0]
+    out = {"dx": np.zeros((T, d_in)), "dA": np.zeros((r, d_in)), "dB": np.zeros((d_out, r)),
+           "dm": np.zeros(d_out)}
+    rc = load().oracle_backward_through_norm(_ptr(g), _ptr(xx), _ptr(w), _ptr(a), _ptr(b),
+                                             _ptr(_f64(m)), dt, _s(s), T, d_in, d_out, r,
+                                             _ptr(out["dx"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                                             _ptr(out["dm"]))
+    if rc:
+        raise MemoryError("oracle_backward_through_norm failed")
     return out
 
 

@@ -356,8 +356,55 @@ def pin_merge_properties():
         assert np.array_equal(O.merge(W, A, B, m, s, n_in=2 * n), Wm / 2), "merge with n_in"
 
 
+def pin_hand_backward_through_norm():
+    g = load_golden()
+    W, A, B, x, dy = (_t32(g[k]) for k in ("W", "A", "B", "x", "dy"))
+    out = O.backward_through_norm(dy, x, W, A, B, g["m"], 2.0)
+    _close(out["dA"], g["s2.thru.dA"], 1e-14, 1e-14, "hand through-norm dA")
+    _close(out["dB"], g["s2.thru.dB"], 1e-14, 1e-14, "hand through-norm dB")
+    _close(out["dx"], g["s2.dx"], 1e-14, 1e-14, "hand through-norm dx")
+    _close(out["dm"], g["s2.dm"], 1e-14, 1e-14, "hand through-norm dm")
+
+
+def pin_backward_through_norm_autograd():
+    """Through-norm gradients vs torch autograd (fp64 CPU) without detach."""
+    for dtype in (torch.float32, torch.bfloat16):
+        W, A, B, m, x, dy = _rand_module(17, 21, 29, 5, 9, dtype)
+        s = 1.5
+        ref = _autograd(W, A, B, m, x, dy, s, detach=False)
+        out = O.backward_through_norm(dy, x, W, A, B, m, s)
+        for k in ("dx", "dA", "dB", "dm"):
+            _close(out[k], ref[k], 1e-11, 1e-13, f"through-norm autograd {k}")
+
+
+def pin_backward_through_norm_finite_differences():
+    """Central differences of L = sum(dy * y) through oracle.forward with n
+    recomputed from the perturbed A or B (L is no longer linear in them, so
+    the quotient matches the derivative to O(h^2))."""
+    W, A, B, m, x, dy = _rand_module(18, 8, 11, 3, 4)
+    s = 0.75
+    out = O.backward_through_norm(dy, x, W, A, B, m, s)
+    dyy = _np64(dy)
+
+    def L(A_, B_):
+        y, _ = O.forward(x, W, A_, B_, m, s)
+        return float((y * dyy).sum())
+
+    h = 2.0 ** -12
+    for name, idx in (("dA", (1, 6)), ("dA", (2, 0)), ("dB", (5, 1)), ("dB", (0, 2))):
+        pos = 0 if name == "dA" else 1
+        plus, minus = [A.clone(), B.clone()], [A.clone(), B.clone()]
+        plus[pos][idx] += h
+        minus[pos][idx] -= h
+        step = float(plus[pos][idx]) - float(minus[pos][idx])
+        fd = (L(*plus) - L(*minus)) / step
+        _close([fd], [out[name][idx]], 1e-6, 1e-10, f"through-norm finite difference {name}")
+
+
 ALL_PINS = [pin_hand_norm, pin_hand_forward, pin_hand_backward, pin_factored_identity,
             pin_textbook_b0, pin_rank1, pin_orthogonal, pin_forward_b0_exact,
             pin_forward_lora_reduction, pin_forward_scale_invariance, pin_forward_linearity,
             pin_forward_subsets, pin_backward_autograd, pin_backward_finite_differences,
-            pin_compose_reductions, pin_hand_merge, pin_merge_properties]
+            pin_compose_reductions, pin_hand_merge, pin_merge_properties,
+            pin_hand_backward_through_norm, pin_backward_through_norm_autograd,
+            pin_backward_through_norm_finite_differences]

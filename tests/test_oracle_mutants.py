@@ -44,6 +44,14 @@ MUTANTS = {
     "merge_base_only": ("Wm[q * d_in + j] = (m[i] / ni) * v[j];",
                         "Wm[q * d_in + j] = (m[i] / ni) * elem(W, dt, i * d_in + j);"),
     "merge_norm_squared": ("ni = sqrt(ni);", "ni = ni;"),
+    "thru_cn_sign": ("dV[i * d_in + j] = acc - cn[i] * V[i * d_in + j];",
+                     "dV[i * d_in + j] = acc + cn[i] * V[i * d_in + j];"),
+    "thru_cn_power": ("cn[i] = m[i] / (nn[i] * nn[i] * nn[i]) * dyh;",
+                      "cn[i] = m[i] / (nn[i] * nn[i]) * dyh;"),
+    "thru_dB_no_scale": ("dB[i * r + k] = acc * s;", "dB[i * r + k] = acc;"),
+    "thru_dA_double_scale": ("dA[k * d_in + j] = acc * s;", "dA[k * d_in + j] = acc * s * s;"),
+    "thru_dA_uses_W": ("acc += elem(B, dt, i * r + k) * dV[i * d_in + j];",
+                       "acc += elem(B, dt, i * r + k) * elem(W, dt, i * d_in + j);"),
 }
 
 
