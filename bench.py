@@ -20,6 +20,8 @@ Printed JSON line (one):
                timed with HIP events on the launch stream.
   merge_*      dora_merge alone (norm given): the merged inference weight,
                HBM GB/s (read W, write W').
+  bwd_through_norm_us  dora_backward_through_norm (the gradient also through
+               the row norm), back-to-back launches.
   cpu_baseline the fp64 oracle forward on the same module on the host cores,
                on a bounded token sample, extrapolated to the full batch.
 """
@@ -236,6 +238,16 @@ def main():
         out["merge_GBps"] = round(merge_bytes / merge_us / 1e3, 1)
         log(f"merge {merge_us:.1f} us = {merge_bytes / merge_us / 1e3:.0f} GB/s")
         del w_out, ws_m
+
+        # backward with the gradient through the norm (same outputs as the
+        # step's backward plus the norm's term in dA and dB)
+        ws_t = torch.empty(D.dora_backward_through_norm_workspace(T, d_in, d_out, r, 1),
+                           dtype=torch.uint8, device=dev)
+        thru_us = timed(lambda: D.dora_backward_through_norm(
+            t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P, y, ws=ws_t, out=grads))
+        out["bwd_through_norm_us"] = round(thru_us, 1)
+        log(f"backward through the norm {thru_us:.1f} us")
+        del ws_t
 
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         lora = torch.randn(T, d_out, device=dev).bfloat16()

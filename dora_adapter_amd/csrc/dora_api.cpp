@@ -311,6 +311,57 @@ BwdPlan plan_backward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dty
     return b;
 }
 
+// Backward through the norm: the detached plan's dh/dm, Q and dx, then the
+// norm's gradient, with cs = -s m dm / n^2 and cB = cs (.) B:
+//   dA = [Q^T | cB^T] [x ; W] + s (cB^T B) A
+//   dB = s dh^T P + cs (.) (W A^T + s B G),   G = A A^T
+// Every part lands as fp32 slots (split-K partials included) that one
+// fixed-order pass sums and rounds.
+struct ThruPlan {
+    BwdPlan b;
+    GPlan g, da, gs, z, y1, y2;
+    int na, nb, ny;  // fp32 slots of dA, of dB's s dh^T P, of W A^T + s B G
+    size_t o_cs, o_cB, o_gpart, o_gfin, o_gspart, o_gsfin, o_aslots, o_bslots, o_yslots;
+    size_t bytes;
+};
+
+ThruPlan plan_through_norm(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype)
+{
+    const bool bf = dtype == DORA_BF16;
+    ThruPlan p;
+    p.b = plan_backward(T, d_in, d_out, r, dtype);
+    p.g = plan_gemm(bf, nt_shape(r, r, d_in), r * r);
+    p.da = plan_gemm(bf, GemmShape{r, d_in, {T, d_out}, 2, 2,
+                                   dma_mn_operand(T, r) && dma_mn_operand(T, d_in) &&
+                                       dma_mn_operand(d_out, r) && dma_mn_operand(d_out, d_in)},
+                     r * d_in);
+    p.gs = plan_gemm(bf, GemmShape{r, r, {d_out, 0}, 1, 2, dma_mn_operand(d_out, r)}, r * r);
+    p.z = plan_gemm(bf, GemmShape{r, d_in, {r, r}, bf ? 2 : 1, 1,
+                                  dma_operand(r, r) && dma_mn_operand(r, d_in)},
+                    r * d_in);
+    p.y1 = plan_gemm(bf, nt_shape(d_out, r, d_in), d_out * r);
+    p.y2 = plan_gemm(bf, GemmShape{d_out, r, {r, r}, bf ? 2 : 1, 1,
+                                   dma_operand(d_out, r) && dma_mn_operand(r, r)},
+                     d_out * r);
+    p.na = p.da.splits + p.z.splits;
+    p.nb = p.b.dB.splits;
+    p.ny = p.y1.splits + p.y2.splits;
+    Carve cv;
+    cv.off = p.b.bytes;
+    const size_t e = esize(dtype);
+    p.o_cs = cv.take(static_cast<size_t>(d_out) * 4);
+    p.o_cB = cv.take(static_cast<size_t>(d_out) * r * e);
+    p.o_gpart = cv.take(static_cast<size_t>(p.g.splits) * r * r * 4);
+    p.o_gfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);
+    p.o_gspart = cv.take(static_cast<size_t>(p.gs.splits) * r * r * 4);
+    p.o_gsfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);
+    p.o_aslots = cv.take(static_cast<size_t>(p.na) * r * d_in * 4);
+    p.o_bslots = cv.take(static_cast<size_t>(p.nb) * d_out * r * 4);
+    p.o_yslots = cv.take(static_cast<size_t>(p.ny) * d_out * r * 4);
+    p.bytes = cv.off;
+    return p;
+}
+
 // ---------------------------------------------------------------- validation
 struct Range {
     const void *p;
@@ -413,6 +464,20 @@ hipError_t run_gemm(bool bf16, const GPlan &p, GemmArgs a, int layout, bool rows
     a.steps_per_split = p.sps;
     return bf16 ? launch_gemm_bf16(a, layout, p.cfg, rowsq, st)
                 : launch_gemm_f32(a, layout, rowsq, st);
+}
+
+// Product into fp32 slots: split z writes alpha * its partial sum at
+// slots + z * M * N (one slot when unsplit).
+int run_slots(bool bf16, const GPlan &p, GemmArgs a, int layout, float *slots, float alpha,
+              hipStream_t st, const char *what)
+{
+    a.mode = EPI_STORE;
+    a.out = slots;
+    a.ldc = a.N;
+    a.out_f32 = 1;
+    a.alpha = alpha;
+    DORA_LAUNCH(run_gemm(bf16, p, a, layout, false, st), what);
+    return DORA_OK;
 }
 
 GemmArgs seg1(int64_t M, int64_t N, const void *a, int64_t lda, const void *b, int64_t ldb,
@@ -724,6 +789,116 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
     // 5. dA = Q^T x  (both MN-major, K = T).
     DORA_CHECK(run_store(bf, p.dA, seg1(r, d_in, Q, r, x, d_in, T), 2, dA, d_in, 1.0f,
                          reinterpret_cast<float *>(w + p.o_dApart), st, "dA"));
+    return DORA_OK;
+}
+
+size_t dora_backward_through_norm_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                            int dtype)
+{
+    if (check_dtype(dtype) || check_dims(dtype, T, d_in, d_out, r))
+        return 0;
+    return plan_through_norm(T, d_in, d_out, r, dtype).bytes;
+}
+
+int dora_backward_through_norm(const void *dy, const void *x, const void *W, const void *A,
+                               const void *B, const float *m, const float *n, float s,
+                               const void *P, const void *y, int64_t T, int64_t d_in,
+                               int64_t d_out, int64_t r, int dtype, void *dx, void *dA, void *dB,
+                               float *dm, void *ws, size_t ws_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_dims(dtype, T, d_in, d_out, r));
+    const bool has_t = T > 0;
+    DORA_CHECK(check_ptrs({{dy, "dy", has_t}, {x, "x", has_t}, {W, "W", true}, {A, "A", true},
+                           {B, "B", true}, {m, "m", true}, {n, "n", true}, {P, "P", has_t},
+                           {y, "y", has_t}, {dx, "dx", has_t}, {dA, "dA", true}, {dB, "dB", true},
+                           {dm, "dm", true}}));
+    const ThruPlan p = plan_through_norm(T, d_in, d_out, r, dtype);
+    DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
+    const bool bf = dtype == DORA_BF16;
+    const size_t e = esize(dtype);
+    DORA_CHECK(check_disjoint(
+        {{{dx, T * d_in * e}, "dx"}, {{dA, r * d_in * e}, "dA"}, {{dB, d_out * r * e}, "dB"},
+         {{dm, d_out * sizeof(float)}, "dm"}, {{ws, p.bytes}, "workspace"}},
+        {{{dy, T * d_out * e}, "dy"}, {{x, T * d_in * e}, "x"}, {{W, d_out * d_in * e}, "W"},
+         {{A, r * d_in * e}, "A"}, {{B, d_out * r * e}, "B"}, {{m, d_out * sizeof(float)}, "m"},
+         {{n, d_out * sizeof(float)}, "n"}, {{P, T * r * e}, "P"}, {{y, T * d_out * e}, "y"}}));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    const BwdPlan &b = p.b;
+    void *dh = w + b.o_dh;
+    float *dmpart = reinterpret_cast<float *>(w + b.o_dmpart);
+    void *Q = w + b.o_Q;
+    float *cs = reinterpret_cast<float *>(w + p.o_cs);
+    void *cB = w + p.o_cB;
+    float *aslots = reinterpret_cast<float *>(w + p.o_aslots);
+    float *bslots = reinterpret_cast<float *>(w + p.o_bslots);
+    float *yslots = reinterpret_cast<float *>(w + p.o_yslots);
+    const size_t gsz = bf ? static_cast<size_t>(r) * r * 2 : 0;  // lo half of a hi/lo pair
+
+    // 1-3. As with n held constant: dh = g dy and dm, Q = s dh B, dx = [dh | Q] [W ; A].
+    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, b.t_chunk, dh, dmpart, st), "dh/dm");
+    DORA_LAUNCH(launch_dm_finish(dmpart, b.nchunks, m, d_out, dm, st), "dm finish");
+    DORA_CHECK(run_store(bf, b.q, seg1(T, r, dh, d_out, B, r, d_out), 1, Q, r, s,
+                         reinterpret_cast<float *>(w + b.o_Qpart), st, "Q = s dh B"));
+    {
+        GemmArgs g = seg1(T, d_in, dh, d_out, W, d_in, d_out);
+        g.seg[1] = GemmSeg{Q, r, A, d_in, r};
+        g.nseg = 2;
+        DORA_CHECK(run_store(bf, b.dx, g, 1, dx, d_in, 1.0f,
+                             reinterpret_cast<float *>(w + b.o_dxpart), st, "dx"));
+    }
+    // 4. The norm's row coefficient cs = -s m dm / n^2 and cB = cs (.) B.
+    DORA_LAUNCH(launch_norm_grad_coef(bf, m, dm, n, s, B, d_out, r, cs, cB, st), "norm grad coef");
+    // 5. dA = [Q^T | cB^T] [x ; W] + s (cB^T B) A.
+    {
+        GemmArgs g = seg1(r, d_in, cB, r, W, d_in, d_out);
+        if (T > 0) {
+            g.seg[1] = g.seg[0];
+            g.seg[0] = GemmSeg{Q, r, x, d_in, T};
+            g.nseg = 2;
+        }
+        DORA_CHECK(run_slots(bf, p.da, g, 2, aslots, 1.0f, st, "dA: Q^T x + cB^T W"));
+        float *gspart = reinterpret_cast<float *>(w + p.o_gspart);
+        char *gs = w + p.o_gsfin;
+        DORA_CHECK(run_slots(bf, p.gs, seg1(r, r, cB, r, B, r, d_out), 2, gspart, 1.0f, st,
+                             "dA: cB^T B"));
+        DORA_LAUNCH(launch_gram_finalize(bf, gspart, p.gs.splits, r, gs, st), "dA: cB^T B sum");
+        GemmArgs z = seg1(r, d_in, gs, r, A, d_in, r);
+        if (bf) {
+            z.seg[1] = GemmSeg{gs + gsz, r, A, d_in, r};
+            z.nseg = 2;
+        }
+        DORA_CHECK(run_slots(bf, p.z, z, 1, aslots + static_cast<size_t>(p.da.splits) * r * d_in,
+                             s, st, "dA: s (cB^T B) A"));
+        DORA_LAUNCH(launch_combine_rows(bf, aslots, p.da.splits,
+                                        aslots + static_cast<size_t>(p.da.splits) * r * d_in,
+                                        p.z.splits, nullptr, r, d_in, dA, st),
+                    "dA combine");
+    }
+    // 6. dB = s dh^T P + cs (.) (W A^T + s B G),  G = A A^T.
+    {
+        DORA_CHECK(run_slots(bf, b.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, bslots, s, st,
+                             "dB: s dh^T P"));
+        float *gpart = reinterpret_cast<float *>(w + p.o_gpart);
+        char *G = w + p.o_gfin;
+        DORA_CHECK(run_slots(bf, p.g, seg1(r, r, A, d_in, A, d_in, d_in), 0, gpart, 1.0f, st,
+                             "dB: A A^T"));
+        DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, G, st), "dB: A A^T sum");
+        DORA_CHECK(run_slots(bf, p.y1, seg1(d_out, r, W, d_in, A, d_in, d_in), 0, yslots, 1.0f,
+                             st, "dB: W A^T"));
+        GemmArgs g = seg1(d_out, r, B, r, G, r, r);
+        if (bf) {
+            g.seg[1] = GemmSeg{B, r, G + gsz, r, r};
+            g.nseg = 2;
+        }
+        DORA_CHECK(run_slots(bf, p.y2, g, 1, yslots + static_cast<size_t>(p.y1.splits) * d_out * r,
+                             s, st, "dB: s B G"));
+        DORA_LAUNCH(launch_combine_rows(bf, bslots, p.nb, yslots, p.ny, cs, d_out, r, dB, st),
+                    "dB combine");
+    }
     return DORA_OK;
 }
 

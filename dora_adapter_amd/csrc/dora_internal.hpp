@@ -105,6 +105,15 @@ hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const f
                                 void *dh, float *dm_part, hipStream_t st);
 hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, int64_t d_out,
                             float *dm, hipStream_t st);
+// Backward through the norm: cs = -s m dm / n^2 per row and cB = cs (.) B.
+hipError_t launch_norm_grad_coef(int bf16, const float *m, const float *dm, const float *n, float s,
+                                 const void *B, int64_t d_out, int64_t r, float *cs, void *cB,
+                                 hipStream_t st);
+// out = sum_z part[z] + rowscale (.) sum_u ypart[u] ([M, N] fp32 slots; rowscale
+// nullable = 1), fixed order, rounded once to the element type.
+hipError_t launch_combine_rows(int bf16, const float *part, int np, const float *ypart, int ny,
+                               const float *rowscale, int64_t M, int64_t N, void *out,
+                               hipStream_t st);
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st);
 hipError_t launch_scale(int bf16, const void *src, float s, int64_t n, void *dst, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);

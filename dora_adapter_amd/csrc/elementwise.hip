@@ -301,6 +301,46 @@ __global__ void gram_finalize_kernel(const float *__restrict__ part, int splits,
     }
 }
 
+// Backward through the norm: cs_i = -s m_i dm_i / n_i^2 (the row
+// coefficient of the norm's gradient, times -s) and cB = cs (.) B.
+template <typename T>
+__global__ void norm_grad_coef_kernel(const float *__restrict__ m, const float *__restrict__ dm,
+                                      const float *__restrict__ n, float s,
+                                      const T *__restrict__ B, int64_t d_out, int64_t r,
+                                      float *__restrict__ cs, T *__restrict__ cB)
+{
+    const int64_t total = d_out * r;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t i = e / r;
+        const float c = -s * m[i] * dm[i] / (n[i] * n[i]);
+        if (e % r == 0)
+            cs[i] = c;
+        Vec8<T>::store1(cB + e, c * Vec8<T>::load1(B + e));
+    }
+}
+
+// out[i, j] = sum_z part[z][i, j] + f_i sum_u ypart[u][i, j] (f_i = rowscale[i],
+// or 1), in this fixed order, rounded once.
+template <typename T>
+__global__ void combine_rows_kernel(const float *__restrict__ part, int np,
+                                    const float *__restrict__ ypart, int ny,
+                                    const float *__restrict__ rowscale, int64_t M, int64_t N,
+                                    T *__restrict__ out)
+{
+    const int64_t MN = M * N;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < MN;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float a = 0.f, y = 0.f;
+        for (int z = 0; z < np; ++z)
+            a += part[static_cast<int64_t>(z) * MN + e];
+        for (int u = 0; u < ny; ++u)
+            y += ypart[static_cast<int64_t>(u) * MN + e];
+        const float f = rowscale != nullptr ? rowscale[e / N] : 1.f;
+        Vec8<T>::store1(out + e, __fmaf_rn(f, y, a));
+    }
+}
+
 // n_i = sqrt(max(base + 2 s cross + s^2 gram, 0)) from fixed-order sums of
 // the per-split / per-tile partials, combined in fp64.
 __global__ void norm_finish_kernel(const float *__restrict__ bp, int zb, const float *__restrict__ cp,
@@ -484,6 +524,45 @@ hipError_t launch_norm_finish(const float *base_part, int zb, const float *cross
         return hipSuccess;
     hipLaunchKernelGGL(norm_finish_kernel, dim3(blocks_for(d_out)), dim3(EW_THREADS), 0, st,
                        base_part, zb, cross_part, zc, gram_part, zg, d_out, s, n, base, cross, gram);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_grad_coef(int bf16, const float *m, const float *dm, const float *n, float s,
+                                 const void *B, int64_t d_out, int64_t r, float *cs, void *cB,
+                                 hipStream_t st)
+{
+    if (d_out == 0)
+        return hipSuccess;
+    int64_t blocks = (d_out * r + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 8192)
+        blocks = 8192;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (bf16)
+        hipLaunchKernelGGL(norm_grad_coef_kernel<uint16_t>, grid, dim3(EW_THREADS), 0, st, m, dm, n,
+                           s, static_cast<const uint16_t *>(B), d_out, r, cs,
+                           static_cast<uint16_t *>(cB));
+    else
+        hipLaunchKernelGGL(norm_grad_coef_kernel<float>, grid, dim3(EW_THREADS), 0, st, m, dm, n, s,
+                           static_cast<const float *>(B), d_out, r, cs, static_cast<float *>(cB));
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_rows(int bf16, const float *part, int np, const float *ypart, int ny,
+                               const float *rowscale, int64_t M, int64_t N, void *out,
+                               hipStream_t st)
+{
+    if (M == 0 || N == 0)
+        return hipSuccess;
+    int64_t blocks = (M * N + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 8192)
+        blocks = 8192;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (bf16)
+        hipLaunchKernelGGL(combine_rows_kernel<uint16_t>, grid, dim3(EW_THREADS), 0, st, part, np,
+                           ypart, ny, rowscale, M, N, static_cast<uint16_t *>(out));
+    else
+        hipLaunchKernelGGL(combine_rows_kernel<float>, grid, dim3(EW_THREADS), 0, st, part, np,
+                           ypart, ny, rowscale, M, N, static_cast<float *>(out));
     return hipGetLastError();
 }
 

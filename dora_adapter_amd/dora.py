@@ -22,7 +22,7 @@ STATUS = {0: "DORA_OK", 1: "DORA_E_NULL", 2: "DORA_E_SHAPE", 3: "DORA_E_DTYPE",
 EXPORTS = ("dora_strerror", "dora_last_error", "dora_norm_workspace", "dora_forward_workspace",
            "dora_backward_workspace", "dora_factored_norm", "dora_compose", "dora_forward",
            "dora_backward", "dora_linear_workspace", "dora_linear", "dora_merge_workspace",
-           "dora_merge")
+           "dora_merge", "dora_backward_through_norm_workspace", "dora_backward_through_norm")
 
 _lib = None
 
@@ -62,6 +62,10 @@ def lib():
         L.dora_backward.restype = c_int
         L.dora_backward.argtypes = [p, p, p, p, p, p, p, f, p, p, i64, i64, i64, i64, c_int, p,
                                     p, p, p, p, sz, p]
+        L.dora_backward_through_norm_workspace.restype = sz
+        L.dora_backward_through_norm_workspace.argtypes = [i64, i64, i64, i64, c_int]
+        L.dora_backward_through_norm.restype = c_int
+        L.dora_backward_through_norm.argtypes = L.dora_backward.argtypes
         L.dora_linear_workspace.restype = sz
         L.dora_linear_workspace.argtypes = [i64, i64, i64, c_int]
         L.dora_linear.restype = c_int
@@ -117,6 +121,15 @@ def dora_backward_workspace(T, d_in, d_out, r, dtype):
     return lib().dora_backward_workspace(T, d_in, d_out, r, dtype)
 
 
+def dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype):
+    return lib().dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype)
+
+
+def dora_backward_through_norm(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None):
+    """Backward with the gradient flowing through the row norm."""
+    return dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=ws, out=out, through_norm=True)
+
+
 def dora_factored_norm(W, A, B, s, terms=False, ws=None, n=None):
     """Row norms of W + s*B*A (fp32 [d_out]); with terms=True also returns
     (base, cross, gram)."""
@@ -165,8 +178,9 @@ def dora_forward(x, W, A, B, m, s, n_in=None, want_P=True, ws=None, y=None, n_ou
     return y, n_out, (P_out if want_P else None)
 
 
-def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None):
-    """Norm-detached backward.  Returns dict(dx, dA, dB, dm)."""
+def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None, through_norm=False):
+    """Backward; returns dict(dx, dA, dB, dm).  The norm is detached unless
+    through_norm is set (then dA and dB include the path through n)."""
     dev = _dev(W)
     T, d_in = x.shape
     d_out = W.shape[0]
@@ -177,12 +191,14 @@ def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None):
                "dA": torch.empty(r, d_in, dtype=W.dtype, device=dev),
                "dB": torch.empty(d_out, r, dtype=W.dtype, device=dev),
                "dm": torch.empty(d_out, dtype=torch.float32, device=dev)}
-    need = lib().dora_backward_workspace(T, d_in, d_out, r, dt)
+    L = lib()
+    size, call = ((L.dora_backward_through_norm_workspace, L.dora_backward_through_norm)
+                  if through_norm else (L.dora_backward_workspace, L.dora_backward))
+    need = size(T, d_in, d_out, r, dt)
     ws = _ws(need, dev) if ws is None else ws
-    _check(lib().dora_backward(_ptr(dy), _ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), _ptr(n),
-                               float(s), _ptr(P), _ptr(y), T, d_in, d_out, r, dt, _ptr(out["dx"]),
-                               _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dm"]), _ptr(ws),
-                               ws.numel(), _stream(dev)))
+    _check(call(_ptr(dy), _ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), _ptr(n), float(s),
+                _ptr(P), _ptr(y), T, d_in, d_out, r, dt, _ptr(out["dx"]), _ptr(out["dA"]),
+                _ptr(out["dB"]), _ptr(out["dm"]), _ptr(ws), ws.numel(), _stream(dev)))
     return out
 
 

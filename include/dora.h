@@ -176,6 +176,32 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
                   void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * dora_backward_through_norm - the same gradients without the stop-gradient:
+ * the gradient also flows through the row norm n = ||W + s B A|| into A and
+ * B.  The DoRA summary page ("Statistical analysis", analysis design) names
+ * the gradient with respect to the direction V and the magnitude as derived
+ * in the method's gradient analysis; the plain chain rule through n_i =
+ * ||V_i|| (dn_i / dV_i = V_i / n_i) gives, with c_i = m_i dm_i / n_i^2,
+ *     dV = dh^T x - diag(c) V
+ *     dA = s B^T dV = Q^T x - s (c (.) B)^T W - s^2 ((c (.) B)^T B) A
+ *     dB = s dV A^T = s dh^T P - s c (.) (W A^T + s B (A A^T))
+ * using only [d_out, r] and [r, r] intermediates (no dense V or B A, as in
+ * the factored norm of the "Scaling DoRA" abstract).  dx and dm are those of
+ * dora_backward, bit for bit.  Arguments, layouts, aliasing rules and the
+ * T = 0 case (dm zero, dA and dB then zero as well) are those of
+ * dora_backward; n is the norm dora_forward returned and is taken as the
+ * exact norm of W + s B A.
+ *   ws: dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype) bytes.
+ */
+size_t dora_backward_through_norm_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                            int dtype);
+int dora_backward_through_norm(const void *dy, const void *x, const void *W, const void *A,
+                               const void *B, const float *m, const float *n, float s,
+                               const void *P, const void *y, int64_t T, int64_t d_in,
+                               int64_t d_out, int64_t r, int dtype, void *dx, void *dA, void *dB,
+                               float *dm, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * dora_merge - the merged weight W' = g (.) (W + s B A), g = m / n by rows,
  * for inference: the DoRA summary pages ("Method"; Key Points 3 and 5) note
  * that the adapted weight folds into the base weight, so inference is a

@@ -157,10 +157,12 @@ def test_forward_validation(kw, code):
     assert _fwd(**kw) == code
 
 
-def test_backward_validation():
+@pytest.mark.parametrize("name", ["dora_backward", "dora_backward_through_norm"])
+def test_backward_validation(name):
     L = D.lib()
     T, d_in, d_out, r = 16, 128, 64, 8
-    need = L.dora_backward_workspace(T, d_in, d_out, r, BF16)
+    need = getattr(L, name + "_workspace")(T, d_in, d_out, r, BF16)
+    fn = getattr(L, name)
     base = [FAKE + (k << 32) for k in range(16)]
 
     def call(**kw):
@@ -168,10 +170,10 @@ def test_backward_validation():
                  P=base[7], y=base[8], dx=base[9], dA=base[10], dB=base[11], dm=base[12],
                  ws=base[13], ws_bytes=need, T=T)
         a.update(kw)
-        return L.dora_backward(_p(a["dy"]), _p(a["x"]), _p(a["W"]), _p(a["A"]), _p(a["B"]),
-                               _p(a["m"]), _p(a["n"]), 1.0, _p(a["P"]), _p(a["y"]), a["T"], d_in,
-                               d_out, r, BF16, _p(a["dx"]), _p(a["dA"]), _p(a["dB"]), _p(a["dm"]),
-                               _p(a["ws"]), a["ws_bytes"], None)
+        return fn(_p(a["dy"]), _p(a["x"]), _p(a["W"]), _p(a["A"]), _p(a["B"]), _p(a["m"]),
+                  _p(a["n"]), 1.0, _p(a["P"]), _p(a["y"]), a["T"], d_in, d_out, r, BF16,
+                  _p(a["dx"]), _p(a["dA"]), _p(a["dB"]), _p(a["dm"]), _p(a["ws"]), a["ws_bytes"],
+                  None)
 
     assert call(dy=0) == E_NULL
     assert call(dm=0) == E_NULL
@@ -180,6 +182,23 @@ def test_backward_validation():
     assert call(dx=base[0]) == E_ALIAS                  # dx over dy
     assert call(dB=base[10] + 64) == E_ALIAS            # dB inside dA
     assert call(T=-1) == E_SHAPE
+    assert call(ws=base[2] + 64) == E_ALIAS             # workspace inside W
+
+
+def test_through_norm_workspace_has_no_dense_term():
+    """The backward through the norm adds only [d_out, r] and [r, d_in] fp32
+    slots and [r, r] Gram terms to the detached backward's workspace: no
+    [d_out, d_in] buffer (V or B A is never formed)."""
+    L = D.lib()
+    r = 384
+    for T, d_out, d_in in ((2048, 8192, 8192), (8192, 28672, 8192), (2048, 8192, 65536)):
+        det = L.dora_backward_workspace(T, d_in, d_out, r, BF16)
+        thru = L.dora_backward_through_norm_workspace(T, d_in, d_out, r, BF16)
+        extra = thru - det
+        assert 0 < extra <= 66 * (d_out * r + r * d_in) * 4 + 70 * r * r * 4 + d_out * (4 + 2 * r)
+    # where a dense bf16 [d_out, d_in] buffer would be 1 GiB, the extra is a fraction of it
+    assert (L.dora_backward_through_norm_workspace(2048, 65536, 8192, r, BF16) -
+            L.dora_backward_workspace(2048, 65536, 8192, r, BF16)) < 8192 * 65536 * 2 / 2
 
 
 def _merge(W=FAKE, A=FAKE + (1 << 32), B=FAKE + (2 << 32), m=FAKE + (3 << 32), n_in=0,
