@@ -22,6 +22,12 @@ Printed JSON line (one):
                HBM GB/s (read W, write W').
   bwd_through_norm_us  dora_backward_through_norm (the gradient also through
                the row norm), back-to-back launches.
+  group_norm   the factored norms of all 56 adapted projections of an 8-layer,
+               8B-class decoder (hidden 4096, key/value 1024, MLP 14336,
+               r 384): dora_factored_norm_grouped vs one dora_factored_norm
+               per module (host launch cost included in both).
+  group_forward_qkv  dora_forward_grouped over the query/key/value siblings
+               of one such layer on one x, vs three dora_forward calls.
   cpu_baseline the fp64 oracle forward on the same module on the host cores,
                on a bounded token sample, extrapolated to the full batch.
 """
@@ -41,6 +47,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "base_gemm_traffic.json")
 KERNEL_WARMUP = 3  # untimed launches before each kernel-leg burst
+GROUP_LAYERS = 8   # decoder layers whose 7 projections form the grouped-norm workload
 
 
 def log(*a):
@@ -248,6 +255,42 @@ def main():
         out["bwd_through_norm_us"] = round(thru_us, 1)
         log(f"backward through the norm {thru_us:.1f} us")
         del ws_t
+
+        # many modules: the factored norms of every adapted projection of an
+        # 8-layer, 8B-class decoder (56 modules, r = 384) in grouped launches,
+        # against the same norms module by module (host launch cost included)
+        group = synth.make_group(synth.decoder_layer_shapes() * GROUP_LAYERS, r, seed=5,
+                                 device=dev)
+        gm = [(g["W"], g["A"], g["B"], g["m"], g["s"]) for g in group]
+        ns_g = [torch.empty(W.shape[0], dtype=torch.float32, device=dev) for W, *_ in gm]
+        ws_g = D._ws(D.dora_factored_norm_grouped_workspace(gm, 1), dev)
+        grp_us = timed(lambda: D.dora_factored_norm_grouped(gm, ns=ns_g, ws=ws_g))
+        ws_1 = D._ws(max(D.dora_norm_workspace(W.shape[0], W.shape[1], r, 1)
+                         for W, *_ in gm), dev)
+        one_us = timed(lambda: [D.dora_factored_norm(W, A, B, sg, ws=ws_1, n=nk)
+                                for (W, A, B, _, sg), nk in zip(gm, ns_g)])
+        gf = sum(norm_flops(W.shape[0], W.shape[1], r) for W, *_ in gm)
+        out["group_norm"] = {"modules": len(gm), "grouped_us": round(grp_us, 1),
+                             "per_module_us": round(one_us, 1),
+                             "grouped_mfma_util": round(gf / grp_us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        log(f"norm of {len(gm)} modules: grouped {grp_us:.1f} us, one by one {one_us:.1f} us")
+        # sibling modules on one input: query, key, value of one layer, T tokens
+        xs = torch.randn(T, 4096, device=dev).bfloat16()
+        qkv = gm[:3]
+        ys_g = [torch.empty(T, W.shape[0], dtype=torch.bfloat16, device=dev) for W, *_ in qkv]
+        Ps_g = [torch.empty(T, r, dtype=torch.bfloat16, device=dev) for _ in qkv]
+        ns_q = [torch.empty(W.shape[0], dtype=torch.float32, device=dev) for W, *_ in qkv]
+        ws_q = D._ws(D.dora_forward_grouped_workspace(qkv, T, 1, P_out=Ps_g), dev)
+        fg_us = timed(lambda: D.dora_forward_grouped(xs, qkv, ws=ws_q, ys=ys_g, ns=ns_q, Ps=Ps_g))
+        ws_f1 = D._ws(max(D.dora_forward_workspace(T, 4096, W.shape[0], r, 1) for W, *_ in qkv),
+                      dev)
+        f1_us = timed(lambda: [D.dora_forward(xs, W, A, B, mq, sq, ws=ws_f1, y=yk, n_out=nk,
+                                              P_out=Pk)
+                               for (W, A, B, mq, sq), yk, nk, Pk in zip(qkv, ys_g, ns_q, Ps_g)])
+        out["group_forward_qkv"] = {"tokens": T, "grouped_us": round(fg_us, 1),
+                                    "per_module_us": round(f1_us, 1)}
+        log(f"q/k/v forward: grouped {fg_us:.1f} us, one by one {f1_us:.1f} us")
+        del group, gm, ns_g, ws_g, ws_1, xs, ys_g, Ps_g, ws_q, ws_f1
 
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         lora = torch.randn(T, d_out, device=dev).bfloat16()

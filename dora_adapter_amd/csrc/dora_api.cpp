@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <vector>
 
 #include "../../include/dora.h"
 #include "dora_internal.hpp"
@@ -567,6 +568,484 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
     return DORA_OK;
 }
 
+// The forward's launch sequence (arguments already validated).
+int forward_impl(const void *x, const void *W, const void *A, const void *B, const float *m,
+                 float s, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype, void *y,
+                 float *n_out, void *P_out, const float *n_in, const FwdPlan &p, char *w,
+                 hipStream_t st)
+{
+    const bool bf = dtype == DORA_BF16;
+    // 1. the row norm (factored), unless the caller has it.
+    if (n_in) {
+        if (n_in != n_out)
+            DORA_LAUNCH(launch_copy_f32(n_in, n_out, d_out, st), "copy n_in");
+    } else {
+        DORA_CHECK(norm_impl(W, A, B, s, d_out, d_in, r, dtype, n_out, nullptr, nullptr, nullptr,
+                             p.norm, w, st));
+    }
+    if (T == 0)
+        return DORA_OK;
+    void *P = P_out ? P_out : static_cast<void *>(w + p.o_P);
+    // 2. P = x A^T (kept for the backward).
+    DORA_CHECK(run_store(bf, p.p, seg1(T, r, x, d_in, A, d_in, d_in), 0, P, r, 1.0f,
+                         reinterpret_cast<float *>(w + p.o_Ppart), st, "adapter x A^T"));
+    // 3. s P as the second K segment's operand (P itself when s = 1).
+    const void *sP = P;
+    if (s != 1.0f) {
+        DORA_LAUNCH(launch_scale(bf, P, s, T * r, w + p.o_sP, st), "scale s P");
+        sP = w + p.o_sP;
+    }
+    // 4. y = (m/n) (x W^T + s P B^T): one K-concatenated product; the epilogue
+    //    applies the magnitude scale in the cancellation-safe form and rounds once.
+    {
+        GemmArgs g = seg1(T, d_out, x, d_in, W, d_in, d_in);
+        g.seg[1] = GemmSeg{sP, r, B, r, r};
+        g.nseg = 2;
+        g.mode = EPI_STORE;
+        g.colm = m;
+        g.coln = n_out;
+        if (p.fused.splits <= 1) {
+            g.out = y;
+            g.ldc = d_out;
+            g.out_f32 = bf ? 0 : 1;
+            DORA_LAUNCH(run_gemm(bf, p.fused, g, 0, false, st), "fused forward product");
+        } else {
+            // split-K: fp32 partials of h; the fixed-order sum applies the
+            // same scale and rounds once
+            float *part = reinterpret_cast<float *>(w + p.o_part_fused);
+            g.colm = g.coln = nullptr;
+            g.out = part;
+            g.ldc = d_out;
+            g.out_f32 = 1;
+            DORA_LAUNCH(run_gemm(bf, p.fused, g, 0, false, st), "fused forward product");
+            DORA_LAUNCH(launch_splitk_reduce(bf, part, p.fused.splits, T, d_out, 1.0f, y, st, m,
+                                             n_out),
+                        "fused forward reduce");
+        }
+    }
+    return DORA_OK;
+}
+
+// ----------------------------------------------------------- grouped modules
+// Many modules in few launches: up to kMaxGroup products per GEMM launch
+// (one tile configuration for all of them) and per small-kernel launch.
+
+int in_module(int rc, int i)
+{
+    if (rc != DORA_OK) {
+        char tmp[sizeof g_last_error];
+        snprintf(tmp, sizeof tmp, "module %d: %s", i, g_last_error);
+        memcpy(g_last_error, tmp, sizeof tmp);
+    }
+    return rc;
+}
+
+int check_module(const dora_module &md, int i, int dtype, bool need_m)
+{
+    DORA_CHECK(in_module(check_dims(dtype, 0, md.d_in, md.d_out, md.r), i));
+    return in_module(check_ptrs({{md.W, "W", true}, {md.A, "A", true}, {md.B, "B", true},
+                                 {md.m, "m", need_m}}),
+                     i);
+}
+
+// One grouped launch: tile configuration and a common split count.
+struct GroupGemm {
+    int cfg = -1;
+    int splits = 1;
+};
+
+// Direct-to-LDS configuration for a set of products (every shape must allow
+// it), and the split count when `split` is allowed (fp32 partial or row-dot
+// outputs): the same time model as plan_gemm, summed over the products.
+GroupGemm plan_group(const std::vector<GemmShape> &sh, bool split)
+{
+    GroupGemm best;
+    double best_cost = -1.0;
+    const double cu_flops = 4.0e12;
+    for (const GemmShape &q : sh)
+        if (!q.dma_ok)
+            return best;
+    for (int c = 0; c < gemm_bf16_num_cfgs(); ++c) {
+        const TileCfg t = gemm_bf16_cfg(c);
+        if (!t.dma)
+            continue;
+        bool ok = true;
+        int64_t zmax = split ? 32 : 1;
+        for (const GemmShape &q : sh) {
+            ok = ok && (t.store_ok || q.rowdot) && (!q.rowsq || t.rowsq_ok);
+            int64_t steps = 0;
+            for (int k = 0; k < q.nseg; ++k)
+                steps += (q.K[k] + t.bk - 1) / t.bk;
+            zmax = std::min<int64_t>(zmax, std::max<int64_t>(steps / 8, 1));
+        }
+        if (!ok)
+            continue;
+        const double t_step = 2.0 * t.BM * t.BN * t.bk / (cu_flops * t.rel_speed);
+        for (int64_t z = 1; z <= zmax; ++z) {
+            double work = 0.0, longest = 0.0;
+            int64_t tiles = 0;
+            for (const GemmShape &q : sh) {
+                int64_t steps = 0;
+                for (int k = 0; k < q.nseg; ++k)
+                    steps += (q.K[k] + t.bk - 1) / t.bk;
+                const int64_t tl = ((q.M + t.BM - 1) / t.BM) * ((q.N + t.BN - 1) / t.BN) * z;
+                const double tile_time = static_cast<double>((steps + z - 1) / z) * t_step;
+                tiles += tl;
+                work += tl * tile_time;
+                longest = std::max(longest, tile_time);
+            }
+            const int64_t waves = std::max<int64_t>((tiles + kCUs - 1) / kCUs, 1);
+            const double cost = std::max(work / kCUs, longest) + waves * kWaveOverhead;
+            if (best_cost < 0 || cost < best_cost * 0.97) {
+                best_cost = cost;
+                best.cfg = c;
+                best.splits = static_cast<int>(z);
+            }
+        }
+    }
+    return best;
+}
+
+GPlan as_gplan(const GroupGemm &g, const GemmShape &q)
+{
+    const TileCfg t = gemm_bf16_cfg(g.cfg);
+    GPlan p;
+    p.cfg = g.cfg;
+    p.BM = t.BM;
+    p.BN = t.BN;
+    p.splits = g.splits;
+    int64_t steps = 0;
+    for (int k = 0; k < q.nseg; ++k)
+        steps += (q.K[k] + t.bk - 1) / t.bk;
+    p.sps = (steps + g.splits - 1) / g.splits;
+    p.ntn = static_cast<int>((q.N + t.BN - 1) / t.BN);
+    return p;
+}
+
+// The factored norm of modules [i0, i1) (at most kMaxGroup): G = A A^T of
+// all of them in one launch, the hi/lo rounding in one, the W A^T row dots
+// (with the row sums of squares of W) in one, the B G row dots in one and
+// the finish in one.  fp32 modules, and bf16 ones the direct-to-LDS kernel
+// cannot take, run module by module (norm_impl).
+struct NormChunk {
+    int i0 = 0, i1 = 0;
+    bool grouped = false;
+    GroupGemm g, u, bg;
+    std::vector<GPlan> pg, pu, pbg;
+    std::vector<NormPlan> single;
+    std::vector<size_t> o_gpart, o_gfin, o_base, o_cross, o_gram;
+    size_t bytes = 0;
+};
+
+NormChunk plan_norm_chunk(const dora_module *mods, int i0, int i1, int dtype)
+{
+    NormChunk c;
+    c.i0 = i0;
+    c.i1 = i1;
+    const bool bf = dtype == DORA_BF16;
+    std::vector<GemmShape> sg, su, sbg;
+    for (int i = i0; i < i1; ++i) {
+        const dora_module &md = mods[i];
+        sg.push_back(nt_shape(md.r, md.r, md.d_in));
+        GemmShape us = nt_shape(md.d_out, md.r, md.d_in);
+        us.rowdot = us.rowsq = true;
+        su.push_back(us);
+        GemmShape b{md.d_out, md.r, {md.r, md.r}, 2, 1,
+                    dma_operand(md.d_out, md.r) && dma_mn_operand(md.r, md.r)};
+        b.rowdot = true;
+        sbg.push_back(b);
+    }
+    if (bf) {
+        c.g = plan_group(sg, true);
+        c.u = plan_group(su, true);
+        c.bg = plan_group(sbg, true);
+        c.grouped = c.g.cfg >= 0 && c.u.cfg >= 0 && c.bg.cfg >= 0;
+    }
+    Carve cv;
+    if (!c.grouped) {
+        for (int i = i0; i < i1; ++i) {
+            Carve one;
+            c.single.push_back(plan_norm(mods[i].d_out, mods[i].d_in, mods[i].r, dtype, one));
+            c.bytes = std::max(c.bytes, one.off);
+        }
+        return c;
+    }
+    for (int k = 0; k < i1 - i0; ++k) {
+        const dora_module &md = mods[i0 + k];
+        c.pg.push_back(as_gplan(c.g, sg[k]));
+        c.pu.push_back(as_gplan(c.u, su[k]));
+        c.pbg.push_back(as_gplan(c.bg, sbg[k]));
+        c.o_gpart.push_back(cv.take(static_cast<size_t>(c.g.splits) * md.r * md.r * 4));
+        c.o_gfin.push_back(cv.take(static_cast<size_t>(2) * md.r * md.r * 2));
+        c.o_base.push_back(cv.take(static_cast<size_t>(c.u.splits) * md.d_out * 4));
+        c.o_cross.push_back(
+            cv.take(static_cast<size_t>(c.u.splits) * c.pu.back().ntn * md.d_out * 4));
+        c.o_gram.push_back(
+            cv.take(static_cast<size_t>(c.bg.splits) * c.pbg.back().ntn * md.d_out * 4));
+    }
+    c.bytes = cv.off;
+    return c;
+}
+
+std::vector<NormChunk> plan_norm_group(const dora_module *mods, const std::vector<int> &which,
+                                       int dtype, size_t &bytes)
+{
+    // `which` lists the modules to normalise; chunks are runs of it
+    std::vector<dora_module> sel;
+    for (int i : which)
+        sel.push_back(mods[i]);
+    std::vector<NormChunk> out;
+    bytes = 0;
+    for (int i0 = 0; i0 < static_cast<int>(sel.size()); i0 += kMaxGroup) {
+        const int i1 = std::min<int>(i0 + kMaxGroup, static_cast<int>(sel.size()));
+        out.push_back(plan_norm_chunk(sel.data(), i0, i1, dtype));
+        bytes = std::max(bytes, out.back().bytes);
+    }
+    return out;
+}
+
+int norm_group_impl(const dora_module *mods, const std::vector<int> &which, int dtype,
+                    float *const *n, const std::vector<NormChunk> &chunks, char *ws,
+                    hipStream_t st)
+{
+    const bool bf = dtype == DORA_BF16;
+    for (const NormChunk &c : chunks) {
+        const int cnt = c.i1 - c.i0;
+        if (!c.grouped) {
+            for (int k = 0; k < cnt; ++k) {
+                const int i = which[c.i0 + k];
+                const dora_module &md = mods[i];
+                DORA_CHECK(norm_impl(md.W, md.A, md.B, md.s, md.d_out, md.d_in, md.r, dtype, n[i],
+                                     nullptr, nullptr, nullptr, c.single[k], ws, st));
+            }
+            continue;
+        }
+        GemmGroup gg, gu, gbg;
+        memset(&gg, 0, sizeof gg);
+        memset(&gu, 0, sizeof gu);
+        memset(&gbg, 0, sizeof gbg);
+        ItemGroup<GramItem> fin;
+        ItemGroup<NormFinishItem> nf;
+        memset(&fin, 0, sizeof fin);
+        memset(&nf, 0, sizeof nf);
+        gg.count = gu.count = gbg.count = fin.count = nf.count = cnt;
+        for (int k = 0; k < cnt; ++k) {
+            const dora_module &md = mods[which[c.i0 + k]];
+            const int64_t r = md.r, d_in = md.d_in, d_out = md.d_out;
+            float *gpart = reinterpret_cast<float *>(ws + c.o_gpart[k]);
+            void *gfin = ws + c.o_gfin[k];
+            float *bpart = reinterpret_cast<float *>(ws + c.o_base[k]);
+            float *cpart = reinterpret_cast<float *>(ws + c.o_cross[k]);
+            float *gmpart = reinterpret_cast<float *>(ws + c.o_gram[k]);
+            // G = A A^T (fp32 split partials)
+            GemmArgs &g = gg.p[k];
+            g = seg1(r, r, md.A, d_in, md.A, d_in, d_in);
+            g.mode = EPI_STORE;
+            g.out = gpart;
+            g.ldc = r;
+            g.out_f32 = 1;
+            g.splits = c.pg[k].splits;
+            g.steps_per_split = c.pg[k].sps;
+            fin.it[k] = GramItem{gpart, gfin, c.pg[k].splits, r};
+            // W A^T row dots against B, row sums of squares of W
+            GemmArgs &u = gu.p[k];
+            u = seg1(d_out, r, md.W, d_in, md.A, d_in, d_in);
+            u.mode = EPI_ROWDOT;
+            u.E = md.B;
+            u.lde = r;
+            u.rowdot = cpart;
+            u.rowsq = bpart;
+            u.splits = c.pu[k].splits;
+            u.steps_per_split = c.pu[k].sps;
+            // B [G_hi ; G_lo] row dots against B
+            GemmArgs &b = gbg.p[k];
+            b = seg1(d_out, r, md.B, r, gfin, r, r);
+            b.seg[1] = GemmSeg{md.B, r, static_cast<const uint16_t *>(gfin) + r * r, r, r};
+            b.nseg = 2;
+            b.mode = EPI_ROWDOT;
+            b.E = md.B;
+            b.lde = r;
+            b.rowdot = gmpart;
+            b.splits = c.pbg[k].splits;
+            b.steps_per_split = c.pbg[k].sps;
+            nf.it[k] = NormFinishItem{bpart,
+                                      cpart,
+                                      gmpart,
+                                      c.pu[k].splits,
+                                      c.pu[k].splits * c.pu[k].ntn,
+                                      c.pbg[k].splits * c.pbg[k].ntn,
+                                      d_out,
+                                      md.s,
+                                      n[which[c.i0 + k]]};
+        }
+        DORA_LAUNCH(launch_gemm_bf16_grouped(gg, 0, c.g.cfg, false, st), "grouped gram A A^T");
+        DORA_LAUNCH(launch_gram_finalize_grouped(bf, fin, st), "grouped gram finalize");
+        DORA_LAUNCH(launch_gemm_bf16_grouped(gu, 0, c.u.cfg, true, st), "grouped cross W A^T");
+        DORA_LAUNCH(launch_gemm_bf16_grouped(gbg, 1, c.bg.cfg, false, st), "grouped gram B G");
+        DORA_LAUNCH(launch_norm_finish_grouped(nf, st), "grouped norm finish");
+    }
+    return DORA_OK;
+}
+
+// Sibling modules on one input x (for instance the query, key and value
+// projections): the norms as above, then per chunk one launch of all
+// P = x A^T, one of the s P scalings, and one of the fused products
+// [x | sP][W | B]^T with the magnitude epilogue.
+struct FwdGroupChunk {
+    int i0, i1;
+    GroupGemm p, fused;
+    std::vector<GPlan> pp, pf;
+    std::vector<size_t> o_P, o_sP;
+};
+
+struct FwdGroupPlan {
+    std::vector<int> need_norm;
+    std::vector<NormChunk> norm;
+    size_t norm_bytes = 0;
+    std::vector<FwdGroupChunk> chunks;
+    bool grouped = true;
+    std::vector<FwdPlan> single;  // module by module when not grouped
+    size_t bytes = 0;
+};
+
+FwdGroupPlan plan_forward_group(const dora_module *mods, int count, int64_t T, int dtype,
+                                const float *const *n_in, void *const *P_out)
+{
+    FwdGroupPlan f;
+    for (int i = 0; i < count; ++i)
+        if (!n_in || !n_in[i])
+            f.need_norm.push_back(i);
+    f.norm = plan_norm_group(mods, f.need_norm, dtype, f.norm_bytes);
+    const size_t e = esize(dtype);
+    size_t most = 0;
+    for (int i0 = 0; i0 < count; i0 += kMaxGroup) {
+        FwdGroupChunk c;
+        c.i0 = i0;
+        c.i1 = std::min(i0 + kMaxGroup, count);
+        std::vector<GemmShape> sp, sf;
+        for (int i = c.i0; i < c.i1; ++i) {
+            const dora_module &md = mods[i];
+            sp.push_back(nt_shape(T, md.r, md.d_in));
+            sf.push_back(fused_shape(T, md.d_in, md.d_out, md.r));
+        }
+        if (dtype == DORA_BF16) {
+            c.p = plan_group(sp, false);
+            c.fused = plan_group(sf, false);
+        }
+        if (c.p.cfg < 0 || c.fused.cfg < 0)
+            f.grouped = false;
+        Carve cv;
+        for (int k = 0; k < c.i1 - c.i0; ++k) {
+            const dora_module &md = mods[c.i0 + k];
+            if (c.p.cfg >= 0 && c.fused.cfg >= 0) {
+                c.pp.push_back(as_gplan(c.p, sp[k]));
+                c.pf.push_back(as_gplan(c.fused, sf[k]));
+            }
+            const bool own_P = !P_out || !P_out[c.i0 + k];
+            c.o_P.push_back(own_P ? cv.take(static_cast<size_t>(T) * md.r * e) : 0);
+            c.o_sP.push_back(md.s != 1.0f ? cv.take(static_cast<size_t>(T) * md.r * e) : 0);
+        }
+        most = std::max(most, cv.off);
+        f.chunks.push_back(c);
+    }
+    f.bytes = align_up(f.norm_bytes) + most;
+    if (!f.grouped) {
+        f.bytes = 0;
+        for (int i = 0; i < count; ++i) {
+            f.single.push_back(plan_forward(T, mods[i].d_in, mods[i].d_out, mods[i].r, dtype));
+            f.bytes = std::max(f.bytes, f.single.back().bytes);
+        }
+    }
+    return f;
+}
+
+int forward_group_impl(const void *x, int64_t T, const dora_module *mods, int count, int dtype,
+                       void *const *y, float *const *n_out, void *const *P_out,
+                       const float *const *n_in, const FwdGroupPlan &f, char *ws, hipStream_t st)
+{
+    const bool bf = dtype == DORA_BF16;
+    if (!f.grouped) {
+        for (int i = 0; i < count; ++i) {
+            const dora_module &md = mods[i];
+            DORA_CHECK(in_module(forward_impl(x, md.W, md.A, md.B, md.m, md.s, T, md.d_in,
+                                              md.d_out, md.r, dtype, y[i], n_out[i],
+                                              P_out ? P_out[i] : nullptr,
+                                              n_in ? n_in[i] : nullptr, f.single[i], ws, st),
+                                 i));
+        }
+        return DORA_OK;
+    }
+    // 1. the norms of every module without a cached one, then the cached ones
+    DORA_CHECK(norm_group_impl(mods, f.need_norm, dtype, n_out, f.norm, ws, st));
+    for (int i = 0; i < count; ++i)
+        if (n_in && n_in[i] && n_in[i] != n_out[i])
+            DORA_LAUNCH(launch_copy_f32(n_in[i], n_out[i], mods[i].d_out, st), "copy n_in");
+    if (T == 0)
+        return DORA_OK;
+    char *w = ws + align_up(f.norm_bytes);
+    for (const FwdGroupChunk &c : f.chunks) {
+        const int cnt = c.i1 - c.i0;
+        GemmGroup gp, gf;
+        ItemGroup<ScaleItem> sc;
+        memset(&gp, 0, sizeof gp);
+        memset(&gf, 0, sizeof gf);
+        memset(&sc, 0, sizeof sc);
+        gp.count = gf.count = cnt;
+        std::vector<const void *> sP(cnt);
+        for (int k = 0; k < cnt; ++k) {
+            const int i = c.i0 + k;
+            const dora_module &md = mods[i];
+            const int64_t d_in = md.d_in, r = md.r;
+            void *P = (P_out && P_out[i]) ? P_out[i] : static_cast<void *>(w + c.o_P[k]);
+            // 2. P = x A^T
+            GemmArgs &g = gp.p[k];
+            g = seg1(T, r, x, d_in, md.A, d_in, d_in);
+            g.mode = EPI_STORE;
+            g.out = P;
+            g.ldc = r;
+            g.out_f32 = bf ? 0 : 1;
+            g.splits = 1;
+            g.steps_per_split = c.pp[k].sps;
+            // 3. s P
+            sP[k] = P;
+            if (md.s != 1.0f) {
+                sc.it[sc.count++] = ScaleItem{P, w + c.o_sP[k], md.s, T * r};
+                sP[k] = w + c.o_sP[k];
+            }
+            // 4. y = (m/n) (x W^T + s P B^T)
+            GemmArgs &h = gf.p[k];
+            h = seg1(T, md.d_out, x, d_in, md.W, d_in, d_in);
+            h.seg[1] = GemmSeg{sP[k], r, md.B, r, r};
+            h.nseg = 2;
+            h.mode = EPI_STORE;
+            h.colm = md.m;
+            h.coln = n_out[i];
+            h.out = y[i];
+            h.ldc = md.d_out;
+            h.out_f32 = bf ? 0 : 1;
+            h.splits = 1;
+            h.steps_per_split = c.pf[k].sps;
+        }
+        DORA_LAUNCH(launch_gemm_bf16_grouped(gp, 0, c.p.cfg, false, st), "grouped x A^T");
+        DORA_LAUNCH(launch_scale_grouped(bf, sc, st), "grouped s P");
+        DORA_LAUNCH(launch_gemm_bf16_grouped(gf, 0, c.fused.cfg, false, st),
+                    "grouped fused forward product");
+    }
+    return DORA_OK;
+}
+
+// Shared validation of the grouped calls' module lists.
+int check_group(const dora_module *mods, int count, int dtype, bool need_m)
+{
+    if (count < 0)
+        return fail(DORA_E_SHAPE, "count=%d is negative", count);
+    if (count > 0 && !mods)
+        return fail(DORA_E_NULL, "modules is NULL");
+    for (int i = 0; i < count; ++i)
+        DORA_CHECK(check_module(mods[i], i, dtype, need_m));
+    return DORA_OK;
+}
+
 }  // namespace
 }  // namespace dora
 
@@ -686,57 +1165,8 @@ int dora_forward(const void *x, const void *W, const void *A, const void *B, con
                               {{rx, "x"}, {rW, "W"}, {rA, "A"}, {rB, "B"}, {rm, "m"}}));
     DORA_CHECK(check_disjoint({{ry, "y"}, {rP, "P_out"}, {rws, "workspace"}}, {{rnin, "n_in"}}));
 
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *w = static_cast<char *>(ws);
-    // 1. the row norm (factored), unless the caller has it.
-    if (n_in) {
-        if (n_in != n_out)
-            DORA_LAUNCH(launch_copy_f32(n_in, n_out, d_out, st), "copy n_in");
-    } else {
-        DORA_CHECK(norm_impl(W, A, B, s, d_out, d_in, r, dtype, n_out, nullptr, nullptr, nullptr,
-                             p.norm, w, st));
-    }
-    if (T == 0)
-        return DORA_OK;
-    void *P = P_out ? P_out : static_cast<void *>(w + p.o_P);
-    // 2. P = x A^T (kept for the backward).
-    DORA_CHECK(run_store(bf, p.p, seg1(T, r, x, d_in, A, d_in, d_in), 0, P, r, 1.0f,
-                         reinterpret_cast<float *>(w + p.o_Ppart), st, "adapter x A^T"));
-    // 3. s P as the second K segment's operand (P itself when s = 1).
-    const void *sP = P;
-    if (s != 1.0f) {
-        DORA_LAUNCH(launch_scale(bf, P, s, T * r, w + p.o_sP, st), "scale s P");
-        sP = w + p.o_sP;
-    }
-    // 4. y = (m/n) (x W^T + s P B^T): one K-concatenated product; the epilogue
-    //    applies the magnitude scale in the cancellation-safe form and rounds once.
-    {
-        GemmArgs g = seg1(T, d_out, x, d_in, W, d_in, d_in);
-        g.seg[1] = GemmSeg{sP, r, B, r, r};
-        g.nseg = 2;
-        g.mode = EPI_STORE;
-        g.colm = m;
-        g.coln = n_out;
-        if (p.fused.splits <= 1) {
-            g.out = y;
-            g.ldc = d_out;
-            g.out_f32 = bf ? 0 : 1;
-            DORA_LAUNCH(run_gemm(bf, p.fused, g, 0, false, st), "fused forward product");
-        } else {
-            // split-K: fp32 partials of h; the fixed-order sum applies the
-            // same scale and rounds once
-            float *part = reinterpret_cast<float *>(w + p.o_part_fused);
-            g.colm = g.coln = nullptr;
-            g.out = part;
-            g.ldc = d_out;
-            g.out_f32 = 1;
-            DORA_LAUNCH(run_gemm(bf, p.fused, g, 0, false, st), "fused forward product");
-            DORA_LAUNCH(launch_splitk_reduce(bf, part, p.fused.splits, T, d_out, 1.0f, y, st, m,
-                                             n_out),
-                        "fused forward reduce");
-        }
-    }
-    return DORA_OK;
+    return forward_impl(x, W, A, B, m, s, T, d_in, d_out, r, dtype, y, n_out, P_out, n_in, p,
+                        static_cast<char *>(ws), static_cast<hipStream_t>(stream));
 }
 
 int dora_backward(const void *dy, const void *x, const void *W, const void *A, const void *B,
@@ -900,6 +1330,127 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
                     "dB combine");
     }
     return DORA_OK;
+}
+
+size_t dora_factored_norm_grouped_workspace(const dora_module *mods, int count, int dtype)
+{
+    if (check_dtype(dtype) || check_group(mods, count, dtype, false))
+        return 0;
+    std::vector<int> all(count);
+    for (int i = 0; i < count; ++i)
+        all[i] = i;
+    size_t bytes = 0;
+    plan_norm_group(mods, all, dtype, bytes);
+    return bytes;
+}
+
+int dora_factored_norm_grouped(const dora_module *mods, int count, int dtype, float *const *n,
+                               void *ws, size_t ws_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_group(mods, count, dtype, false));
+    if (count == 0)
+        return DORA_OK;
+    if (!n)
+        return fail(DORA_E_NULL, "n is NULL");
+    std::vector<int> all(count);
+    for (int i = 0; i < count; ++i)
+        all[i] = i;
+    size_t bytes = 0;
+    const std::vector<NormChunk> chunks = plan_norm_group(mods, all, dtype, bytes);
+    DORA_CHECK(check_ws(ws, ws_bytes, bytes));
+    const size_t e = esize(dtype);
+    const Range rws{ws, bytes};
+    for (int i = 0; i < count; ++i) {
+        const dora_module &md = mods[i];
+        DORA_CHECK(in_module(check_ptrs({{n[i], "n", true}}), i));
+        const Range rn{n[i], md.d_out * sizeof(float)};
+        DORA_CHECK(in_module(check_disjoint({{rws, "workspace"}},
+                                            {{{md.W, md.d_out * md.d_in * e}, "W"},
+                                             {{md.A, md.r * md.d_in * e}, "A"},
+                                             {{md.B, md.d_out * md.r * e}, "B"}, {rn, "n"}}),
+                             i));
+        for (int j = 0; j < count; ++j) {
+            const dora_module &mj = mods[j];
+            DORA_CHECK(in_module(check_disjoint({{rn, "n"}},
+                                                {{{mj.W, mj.d_out * mj.d_in * e}, "a W"},
+                                                 {{mj.A, mj.r * mj.d_in * e}, "an A"},
+                                                 {{mj.B, mj.d_out * mj.r * e}, "a B"}}),
+                                 i));
+            if (j > i && overlap(rn, {n[j], mj.d_out * sizeof(float)}))
+                return fail(DORA_E_ALIAS, "n of modules %d and %d overlap", i, j);
+        }
+    }
+    return norm_group_impl(mods, all, dtype, n, chunks, static_cast<char *>(ws),
+                           static_cast<hipStream_t>(stream));
+}
+
+size_t dora_forward_grouped_workspace(const dora_module *mods, int count, int64_t T,
+                                      int dtype, const float *const *n_in,
+                                      void *const *P_out)
+{
+    if (check_dtype(dtype) || check_group(mods, count, dtype, true) ||
+        check_dims(dtype, T, 8, 8, 8))
+        return 0;
+    return plan_forward_group(mods, count, T, dtype, n_in, P_out).bytes;
+}
+
+int dora_forward_grouped(const void *x, int64_t T, int64_t d_in, const dora_module *mods,
+                         int count, int dtype, void *const *y, float *const *n_out,
+                         void *const *P_out, const float *const *n_in, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    g_last_error[0] = '\0';
+    DORA_CHECK(check_dtype(dtype));
+    DORA_CHECK(check_group(mods, count, dtype, true));
+    DORA_CHECK(check_dims(dtype, T, d_in, 8, 8));
+    if (count == 0)
+        return DORA_OK;
+    const bool has_t = T > 0;
+    DORA_CHECK(check_ptrs({{x, "x", has_t}}));
+    if (!n_out || (has_t && !y))
+        return fail(DORA_E_NULL, "%s is NULL", !n_out ? "n_out" : "y");
+    const FwdGroupPlan f = plan_forward_group(mods, count, T, dtype, n_in, P_out);
+    DORA_CHECK(check_ws(ws, ws_bytes, f.bytes));
+    const size_t e = esize(dtype);
+    const Range rx{x, T * d_in * e}, rws{ws, f.bytes};
+    // every output of every module is disjoint from every input and from the
+    // other outputs (a cached n may be its own n_out)
+    std::vector<Named> outs, ins;
+    outs.push_back({rws, "workspace"});
+    ins.push_back({rx, "x"});
+    for (int i = 0; i < count; ++i) {
+        const dora_module &md = mods[i];
+        if (md.d_in != d_in)
+            return fail(DORA_E_SHAPE, "module %d: d_in=%lld, x has %lld", i, (long long)md.d_in,
+                        (long long)d_in);
+        void *Pi = P_out ? P_out[i] : nullptr;
+        const float *ni = n_in ? n_in[i] : nullptr;
+        DORA_CHECK(in_module(check_ptrs({{y ? y[i] : nullptr, "y", has_t},
+                                         {n_out[i], "n_out", true}, {Pi, "P_out", false},
+                                         {ni, "n_in", false}}),
+                             i));
+        outs.push_back({{y ? y[i] : nullptr, T * md.d_out * e}, "a y"});
+        outs.push_back({{n_out[i], md.d_out * sizeof(float)}, "an n_out"});
+        outs.push_back({{Pi, T * md.r * e}, "a P_out"});
+        ins.push_back({{md.W, md.d_out * d_in * e}, "a W"});
+        ins.push_back({{md.A, md.r * d_in * e}, "an A"});
+        ins.push_back({{md.B, md.d_out * md.r * e}, "a B"});
+        ins.push_back({{md.m, md.d_out * sizeof(float)}, "an m"});
+        if (ni && ni != n_out[i])
+            ins.push_back({{ni, md.d_out * sizeof(float)}, "an n_in"});
+    }
+    for (size_t a = 0; a < outs.size(); ++a) {
+        for (size_t b = a + 1; b < outs.size(); ++b)
+            if (overlap(outs[a].r, outs[b].r))
+                return fail(DORA_E_ALIAS, "%s overlaps %s", outs[a].name, outs[b].name);
+        for (const Named &q : ins)
+            if (overlap(outs[a].r, q.r))
+                return fail(DORA_E_ALIAS, "%s overlaps %s", outs[a].name, q.name);
+    }
+    return forward_group_impl(x, T, mods, count, dtype, y, n_out, P_out, n_in, f,
+                              static_cast<char *>(ws), static_cast<hipStream_t>(stream));
 }
 
 size_t dora_merge_workspace(int64_t d_out, int64_t d_in, int64_t r, int dtype)

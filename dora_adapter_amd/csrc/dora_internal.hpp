@@ -58,12 +58,29 @@ struct GemmArgs {
     float *rowsq;
 };
 
+// Up to kMaxGroup independent products in one launch (passed by value as the
+// kernel argument, so no descriptor table lives in device memory).  Every
+// problem uses the launch's tile configuration and operand layout; problem
+// p owns the linear workgroup ids [tile_start[p], tile_start[p + 1]), i.e.
+// its tiles times its splits.
+constexpr int kMaxGroup = 16;
+struct GemmGroup {
+    GemmArgs p[kMaxGroup];
+    int tile_start[kMaxGroup + 1];
+    int count;
+};
+static_assert(sizeof(GemmGroup) <= 4096, "a group must fit the kernel argument space");
+
 // Launchers (gemm_bf16.hip / gemm_f32.hip).  `layout` selects the operand
 // orders: 0 = A K-major, B K-major (C = A B^T); 1 = A K-major, B MN-major
 // (C = A B); 2 = A MN-major, B MN-major (C = A^T B).  `cfg` picks the tile
 // shape (see gemm_configs in the .hip file).
 hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs &a, int layout, bool rowsq, hipStream_t st);
+// Grouped launch of the pipelined bf16 kernel (cfg must be a direct-to-LDS
+// configuration); tile_start and count are filled in here from the problems'
+// shapes and splits.
+hipError_t launch_gemm_bf16_grouped(GemmGroup &g, int layout, int cfg, bool rowsq, hipStream_t st);
 
 // Tile configurations of the bf16 MFMA GEMM, indexable by `cfg`.  Two
 // kernels: the general one (any shape, operands staged through registers, K
@@ -114,6 +131,36 @@ hipError_t launch_norm_grad_coef(int bf16, const float *m, const float *dm, cons
 hipError_t launch_combine_rows(int bf16, const float *part, int np, const float *ypart, int ny,
                                const float *rowscale, int64_t M, int64_t N, void *out,
                                hipStream_t st);
+// Grouped small kernels: one launch over up to kMaxGroup modules (items
+// passed by value; blockIdx.y selects the item), the same arithmetic as the
+// single-module launchers.
+template <typename Item>
+struct ItemGroup {
+    Item it[kMaxGroup];
+    int count;
+};
+struct GramItem {
+    const float *part;
+    void *G;
+    int splits;
+    int64_t r;
+};
+struct NormFinishItem {
+    const float *bp, *cp, *gp;
+    int zb, zc, zg;
+    int64_t d_out;
+    float s;
+    float *n;
+};
+struct ScaleItem {
+    const void *src;
+    void *dst;
+    float s;
+    int64_t n;
+};
+hipError_t launch_gram_finalize_grouped(int bf16, const ItemGroup<GramItem> &g, hipStream_t st);
+hipError_t launch_norm_finish_grouped(const ItemGroup<NormFinishItem> &g, hipStream_t st);
+hipError_t launch_scale_grouped(int bf16, const ItemGroup<ScaleItem> &g, hipStream_t st);
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st);
 hipError_t launch_scale(int bf16, const void *src, float s, int64_t n, void *dst, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);

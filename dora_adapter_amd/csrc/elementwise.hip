@@ -281,8 +281,8 @@ __global__ void splitk_reduce_kernel(const float *__restrict__ part, int splits,
 // [0, r) and G_lo = bf16(G - G_hi) into rows [r, 2r) of a [2r, r] matrix, so
 // that B G = B G_hi + B G_lo keeps about 16 bits of G on bf16 MFMAs.
 // fp32: writes G itself.
-__global__ void gram_finalize_kernel(const float *__restrict__ part, int splits, int64_t r, int bf16,
-                                     void *__restrict__ G_out)
+__device__ __forceinline__ void gram_finalize_all(const float *__restrict__ part, int splits,
+                                                  int64_t r, int bf16, void *__restrict__ G_out)
 {
     const int64_t rr = r * r;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < rr;
@@ -299,6 +299,19 @@ __global__ void gram_finalize_kernel(const float *__restrict__ part, int splits,
             static_cast<float *>(G_out)[e] = acc;
         }
     }
+}
+
+__global__ void gram_finalize_kernel(const float *__restrict__ part, int splits, int64_t r, int bf16,
+                                     void *__restrict__ G_out)
+{
+    gram_finalize_all(part, splits, r, bf16, G_out);
+}
+
+// One module of a group per blockIdx.y.
+__global__ void gram_finalize_grouped_kernel(ItemGroup<GramItem> g, int bf16)
+{
+    const GramItem &it = g.it[blockIdx.y];
+    gram_finalize_all(it.part, it.splits, it.r, bf16, it.G);
 }
 
 // Backward through the norm: cs_i = -s m_i dm_i / n_i^2 (the row
@@ -343,14 +356,12 @@ __global__ void combine_rows_kernel(const float *__restrict__ part, int np,
 
 // n_i = sqrt(max(base + 2 s cross + s^2 gram, 0)) from fixed-order sums of
 // the per-split / per-tile partials, combined in fp64.
-__global__ void norm_finish_kernel(const float *__restrict__ bp, int zb, const float *__restrict__ cp,
-                                   int zc, const float *__restrict__ gp, int zg, int64_t d_out,
-                                   float s, float *__restrict__ n, float *base, float *cross,
-                                   float *gram)
+__device__ __forceinline__ void norm_finish_row(int64_t i, const float *__restrict__ bp, int zb,
+                                                const float *__restrict__ cp, int zc,
+                                                const float *__restrict__ gp, int zg,
+                                                int64_t d_out, float s, float *__restrict__ n,
+                                                float *base, float *cross, float *gram)
 {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= d_out)
-        return;
     double b = 0.0, c = 0.0, g = 0.0;
     for (int z = 0; z < zb; ++z)
         b += bp[static_cast<int64_t>(z) * d_out + i];
@@ -371,12 +382,42 @@ __global__ void norm_finish_kernel(const float *__restrict__ bp, int zb, const f
         gram[i] = static_cast<float>(g);
 }
 
+__global__ void norm_finish_kernel(const float *__restrict__ bp, int zb, const float *__restrict__ cp,
+                                   int zc, const float *__restrict__ gp, int zg, int64_t d_out,
+                                   float s, float *__restrict__ n, float *base, float *cross,
+                                   float *gram)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < d_out)
+        norm_finish_row(i, bp, zb, cp, zc, gp, zg, d_out, s, n, base, cross, gram);
+}
+
+__global__ void norm_finish_grouped_kernel(ItemGroup<NormFinishItem> g)
+{
+    const NormFinishItem &it = g.it[blockIdx.y];
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < it.d_out;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        norm_finish_row(i, it.bp, it.zb, it.cp, it.zc, it.gp, it.zg, it.d_out, it.s, it.n, nullptr,
+                        nullptr, nullptr);
+}
+
 template <typename T>
 __global__ void scale_kernel(const T *__restrict__ src, float s, int64_t n, T *__restrict__ dst)
 {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
         Vec8<T>::store1(dst + i, s * Vec8<T>::load1(src + i));
+}
+
+template <typename T>
+__global__ void scale_grouped_kernel(ItemGroup<ScaleItem> g)
+{
+    const ScaleItem &it = g.it[blockIdx.y];
+    const T *src = static_cast<const T *>(it.src);
+    T *dst = static_cast<T *>(it.dst);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < it.n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        Vec8<T>::store1(dst + i, it.s * Vec8<T>::load1(src + i));
 }
 
 __global__ void copy_f32_kernel(const float *__restrict__ src, float *__restrict__ dst, int64_t n)
@@ -563,6 +604,53 @@ hipError_t launch_combine_rows(int bf16, const float *part, int np, const float 
     else
         hipLaunchKernelGGL(combine_rows_kernel<float>, grid, dim3(EW_THREADS), 0, st, part, np,
                            ypart, ny, rowscale, M, N, static_cast<float *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_gram_finalize_grouped(int bf16, const ItemGroup<GramItem> &g, hipStream_t st)
+{
+    int64_t most = 0;
+    for (int k = 0; k < g.count; ++k)
+        most = most > g.it[k].r * g.it[k].r ? most : g.it[k].r * g.it[k].r;
+    if (g.count == 0 || most == 0)
+        return hipSuccess;
+    int64_t blocks = (most + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 1024)
+        blocks = 1024;
+    hipLaunchKernelGGL(gram_finalize_grouped_kernel,
+                       dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(g.count)),
+                       dim3(EW_THREADS), 0, st, g, bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_finish_grouped(const ItemGroup<NormFinishItem> &g, hipStream_t st)
+{
+    int64_t most = 0;
+    for (int k = 0; k < g.count; ++k)
+        most = most > g.it[k].d_out ? most : g.it[k].d_out;
+    if (g.count == 0 || most == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(norm_finish_grouped_kernel,
+                       dim3(blocks_for(most), static_cast<unsigned>(g.count)), dim3(EW_THREADS), 0,
+                       st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_grouped(int bf16, const ItemGroup<ScaleItem> &g, hipStream_t st)
+{
+    int64_t most = 0;
+    for (int k = 0; k < g.count; ++k)
+        most = most > g.it[k].n ? most : g.it[k].n;
+    if (g.count == 0 || most == 0)
+        return hipSuccess;
+    int64_t blocks = (most + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 4096)
+        blocks = 4096;
+    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(g.count));
+    if (bf16)
+        hipLaunchKernelGGL(scale_grouped_kernel<uint16_t>, grid, dim3(EW_THREADS), 0, st, g);
+    else
+        hipLaunchKernelGGL(scale_grouped_kernel<float>, grid, dim3(EW_THREADS), 0, st, g);
     return hipGetLastError();
 }
 

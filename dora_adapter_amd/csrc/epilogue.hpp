@@ -236,13 +236,19 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
 // contiguous run of logical tiles, and logical tiles are ordered in groups
 // of 8 tile rows so that the workgroups resident on one XCD at a time share
 // A rows and B columns in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN, int &tm, int &tn)
+__device__ __forceinline__ int xcd_linear_id()
 {
     const int nb = static_cast<int>(gridDim.x);
     const int b = static_cast<int>(blockIdx.x);
     const int q = nb >> 3, rem = nb & 7;
     const int xcd = b & 7, local = b >> 3;
-    const int L = (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+    return (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
+// Tile L of an M x N product in groups of 8 tile rows.
+__device__ __forceinline__ void tile_in_order(int L, int64_t M, int64_t N, int BM, int BN, int &tm,
+                                              int &tn)
+{
     const int num_m = static_cast<int>((M + BM - 1) / BM);
     const int num_n = static_cast<int>((N + BN - 1) / BN);
     constexpr int GROUP = 8;
@@ -253,6 +259,27 @@ __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN
     const int in_g = L - group * per_group;
     tm = first_m + in_g % gsz;
     tn = in_g / gsz;
+}
+
+__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN, int &tm, int &tn)
+{
+    tile_in_order(xcd_linear_id(), M, N, BM, BN, tm, tn);
+}
+
+// Grouped launch: problem p, its tile (tm, tn) and split z of this workgroup
+// (the XCD-aware linear order runs through the problems in turn).
+__device__ __forceinline__ void group_coords(const GemmGroup &grp, int BM, int BN, int &p, int &tm,
+                                             int &tn, int &z)
+{
+    const int L = xcd_linear_id();
+    p = 0;
+    while (p + 1 < grp.count && L >= grp.tile_start[p + 1])
+        ++p;
+    const int64_t M = grp.p[p].M, N = grp.p[p].N;
+    const int tiles = static_cast<int>(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+    const int local = L - grp.tile_start[p];
+    z = local / tiles;
+    tile_in_order(local - z * tiles, M, N, BM, BN, tm, tn);
 }
 
 }  // namespace dora

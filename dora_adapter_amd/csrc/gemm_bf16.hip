@@ -334,6 +334,18 @@ DORA_DMA_INST(128, 128, 2, 2)
 DORA_DMA_INST(128, 384, 1, 4)
 template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 1, 4, true, true, true>(GemmArgs);
 #undef DORA_DMA_INST
+#define DORA_DMA_GROUP_INST(BM, BN, WM, WN)                                                      \
+    template __global__ void dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, true, true, false>( \
+        GemmGroup);                                                                              \
+    template __global__ void dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, true, false, false>( \
+        GemmGroup);
+DORA_DMA_GROUP_INST(256, 256, 2, 2)
+DORA_DMA_GROUP_INST(256, 128, 2, 2)
+DORA_DMA_GROUP_INST(128, 128, 2, 2)
+DORA_DMA_GROUP_INST(128, 384, 1, 4)
+template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 1, 4, true, true, true>(
+    GemmGroup);
+#undef DORA_DMA_GROUP_INST
 
 namespace {
 
@@ -365,6 +377,46 @@ hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStrea
         return launch_dma<BM, BN, WM, WN, true, false, false>(a, st);
     case 2:
         return launch_dma<BM, BN, WM, WN, false, false, false>(a, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
+hipError_t launch_dma_group(GemmGroup &g, hipStream_t st)
+{
+    int64_t total = 0;
+    for (int p = 0; p < g.count; ++p) {
+        g.tile_start[p] = static_cast<int>(total);
+        const GemmArgs &a = g.p[p];
+        total += ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splits;
+    }
+    g.tile_start[g.count] = static_cast<int>(total);
+    if (total == 0)
+        return hipSuccess;
+    if (total > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, AK, BKM, RS>),
+                       dim3(static_cast<unsigned>(total)), dim3(WM * WN * 64), 0, st, g);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_dma_group_layout(GemmGroup &g, int layout, bool rowsq, hipStream_t st)
+{
+    switch (layout) {
+    case 0:
+        if (rowsq) {
+            if constexpr (WM == 1)
+                return launch_dma_group<BM, BN, WM, WN, true, true, true>(g, st);
+            else
+                return hipErrorInvalidValue;
+        }
+        return launch_dma_group<BM, BN, WM, WN, true, true, false>(g, st);
+    case 1:
+        if (rowsq)
+            return hipErrorInvalidValue;
+        return launch_dma_group<BM, BN, WM, WN, true, false, false>(g, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -433,6 +485,28 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
         return launch_dma_layout<128, 128, 2, 2>(a, layout, rowsq, st);
     case 7:
         return launch_dma_layout<128, 384, 1, 4>(a, layout, rowsq, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_bf16_grouped(GemmGroup &g, int layout, int cfg, bool rowsq, hipStream_t st)
+{
+    if (g.count < 1 || g.count > kMaxGroup || cfg < 0 || cfg >= gemm_bf16_num_cfgs() ||
+        !kCfgs[cfg].dma || (rowsq && !kCfgs[cfg].rowsq_ok))
+        return hipErrorInvalidValue;
+    for (int p = 0; p < g.count; ++p)
+        if ((g.p[p].mode != EPI_ROWDOT && !kCfgs[cfg].store_ok) || g.p[p].splits < 1)
+            return hipErrorInvalidValue;
+    switch (cfg) {
+    case 4:
+        return launch_dma_group_layout<256, 256, 2, 2>(g, layout, rowsq, st);
+    case 5:
+        return launch_dma_group_layout<256, 128, 2, 2>(g, layout, rowsq, st);
+    case 6:
+        return launch_dma_group_layout<128, 128, 2, 2>(g, layout, rowsq, st);
+    case 7:
+        return launch_dma_group_layout<128, 384, 1, 4>(g, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }

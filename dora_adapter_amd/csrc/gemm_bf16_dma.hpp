@@ -302,8 +302,10 @@ __device__ __forceinline__ void mfma_one(f32x16_t (&acc)[TM][TN], const Frags<TM
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
 }
 
+// One output tile (tm, tn) of split z of the product g.
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
-__global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
+__device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, const int tn,
+                                              const int z)
 {
     using C = DmaCfg<BM, BN, WM, WN>;
     using DA = OperandDma<AK, BM, WM * WN>;
@@ -322,10 +324,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
     // wave index as a scalar: LDS destinations of the DMA are then SGPR values
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_coords(g.M, g.N, BM, BN, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
-    const int z = static_cast<int>(blockIdx.y);
 
     // stages of the concatenated K range, and this split's share
     const int64_t st1 = (g.seg[0].K + BK - 1) / BK;
@@ -628,6 +627,25 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
             __syncthreads();
         }
     }
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
+__global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
+{
+    int tm, tn;
+    tile_coords(g.M, g.N, BM, BN, tm, tn);
+    gemm_dma_tile<BM, BN, WM, WN, AK, BKM, ROWSQ>(g, tm, tn, static_cast<int>(blockIdx.y));
+}
+
+// Several independent products in one launch (one tile configuration and
+// operand layout): the workgroups of problem p are the linear ids
+// [tile_start[p], tile_start[p + 1]), each problem's tiles x splits.
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
+__global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_grouped_kernel(GemmGroup grp)
+{
+    int p, tm, tn, z;
+    group_coords(grp, BM, BN, p, tm, tn, z);
+    gemm_dma_tile<BM, BN, WM, WN, AK, BKM, ROWSQ>(grp.p[p], tm, tn, z);
 }
 
 }  // namespace dma

@@ -22,9 +22,18 @@ STATUS = {0: "DORA_OK", 1: "DORA_E_NULL", 2: "DORA_E_SHAPE", 3: "DORA_E_DTYPE",
 EXPORTS = ("dora_strerror", "dora_last_error", "dora_norm_workspace", "dora_forward_workspace",
            "dora_backward_workspace", "dora_factored_norm", "dora_compose", "dora_forward",
            "dora_backward", "dora_linear_workspace", "dora_linear", "dora_merge_workspace",
-           "dora_merge", "dora_backward_through_norm_workspace", "dora_backward_through_norm")
+           "dora_merge", "dora_backward_through_norm_workspace", "dora_backward_through_norm",
+           "dora_factored_norm_grouped_workspace", "dora_factored_norm_grouped",
+           "dora_forward_grouped_workspace", "dora_forward_grouped")
 
 _lib = None
+
+
+class DoraModule(ctypes.Structure):
+    """struct dora_module of include/dora.h."""
+    _fields_ = [("W", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("s", ctypes.c_float), ("d_out", ctypes.c_int64),
+                ("d_in", ctypes.c_int64), ("r", ctypes.c_int64)]
 
 
 class DoraError(RuntimeError):
@@ -66,6 +75,15 @@ def lib():
         L.dora_backward_through_norm_workspace.argtypes = [i64, i64, i64, i64, c_int]
         L.dora_backward_through_norm.restype = c_int
         L.dora_backward_through_norm.argtypes = L.dora_backward.argtypes
+        mp = ctypes.POINTER(DoraModule)
+        L.dora_factored_norm_grouped_workspace.restype = sz
+        L.dora_factored_norm_grouped_workspace.argtypes = [mp, c_int, c_int]
+        L.dora_factored_norm_grouped.restype = c_int
+        L.dora_factored_norm_grouped.argtypes = [mp, c_int, c_int, p, p, sz, p]
+        L.dora_forward_grouped_workspace.restype = sz
+        L.dora_forward_grouped_workspace.argtypes = [mp, c_int, i64, c_int, p, p]
+        L.dora_forward_grouped.restype = c_int
+        L.dora_forward_grouped.argtypes = [p, i64, i64, mp, c_int, c_int, p, p, p, p, p, sz, p]
         L.dora_linear_workspace.restype = sz
         L.dora_linear_workspace.argtypes = [i64, i64, i64, c_int]
         L.dora_linear.restype = c_int
@@ -238,3 +256,77 @@ def dora_merge(W, A, B, m, s, n_in=None, out=None, ws=None):
     _check(lib().dora_merge(_ptr(W), _ptr(A), _ptr(B), _ptr(m), float(s), d_out, d_in, r, dt,
                             _ptr(n_in), _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
     return out
+
+
+def _modules(mods):
+    """(W, A, B, m, s) tuples -> a ctypes array of DoraModule."""
+    arr = (DoraModule * max(len(mods), 1))()
+    for k, (W, A, B, m, s) in enumerate(mods):
+        arr[k] = DoraModule(W.data_ptr(), A.data_ptr(), B.data_ptr(),
+                            None if m is None else m.data_ptr(), float(s), W.shape[0],
+                            W.shape[1], A.shape[0])
+    return arr
+
+
+def _ptrs(ts):
+    """Host array of device pointers (None entries stay NULL); None -> NULL."""
+    if ts is None:
+        return None
+    arr = (ctypes.c_void_p * max(len(ts), 1))()
+    for k, t in enumerate(ts):
+        arr[k] = None if t is None else t.data_ptr()
+    return arr
+
+
+def dora_factored_norm_grouped_workspace(mods, dtype):
+    return lib().dora_factored_norm_grouped_workspace(_modules(mods), len(mods), dtype)
+
+
+def dora_forward_grouped_workspace(mods, T, dtype, n_in=None, P_out=None):
+    return lib().dora_forward_grouped_workspace(_modules(mods), len(mods), T, dtype,
+                                                _ptrs(n_in), _ptrs(P_out))
+
+
+def dora_factored_norm_grouped(mods, ns=None, ws=None):
+    """Row norms of W + sBA for every (W, A, B, m, s) in mods (m unused), in
+    grouped launches.  Returns the list of fp32 norms."""
+    if not mods:
+        return []
+    dev = _dev(mods[0][0])
+    dt = _dt(mods[0][0])
+    arr = _modules(mods)
+    ns = [torch.empty(W.shape[0], dtype=torch.float32, device=dev) for W, *_ in mods] \
+        if ns is None else ns
+    need = lib().dora_factored_norm_grouped_workspace(arr, len(mods), dt)
+    ws = _ws(need, dev) if ws is None else ws
+    keep = _ptrs(ns)
+    _check(lib().dora_factored_norm_grouped(arr, len(mods), dt, ctypes.cast(keep, ctypes.c_void_p),
+                                            _ptr(ws), ws.numel(), _stream(dev)))
+    return ns
+
+
+def dora_forward_grouped(x, mods, n_in=None, want_P=True, ws=None, ys=None, ns=None, Ps=None):
+    """dora_forward for sibling modules sharing x.  mods: (W, A, B, m, s)
+    tuples; n_in: optional list of cached norms (entries may be None).
+    Returns (ys, ns, Ps)."""
+    if not mods:
+        return [], [], []
+    dev = _dev(x)
+    T, d_in = x.shape
+    dt = _dt(x)
+    arr = _modules(mods)
+    ys = [torch.empty(T, W.shape[0], dtype=x.dtype, device=dev) for W, *_ in mods] \
+        if ys is None else ys
+    ns = [torch.empty(W.shape[0], dtype=torch.float32, device=dev) for W, *_ in mods] \
+        if ns is None else ns
+    if want_P and Ps is None:
+        Ps = [torch.empty(T, A.shape[0], dtype=x.dtype, device=dev) for _, A, *_ in mods]
+    if not want_P:
+        Ps = None
+    py, pn, pP, pnin = _ptrs(ys), _ptrs(ns), _ptrs(Ps), _ptrs(n_in)
+    vp = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+    need = lib().dora_forward_grouped_workspace(arr, len(mods), T, dt, vp(pnin), vp(pP))
+    ws = _ws(need, dev) if ws is None else ws
+    _check(lib().dora_forward_grouped(_ptr(x), T, d_in, arr, len(mods), dt, vp(py), vp(pn),
+                                      vp(pP), vp(pnin), _ptr(ws), ws.numel(), _stream(dev)))
+    return ys, ns, Ps

@@ -54,7 +54,8 @@ TRAIN_R384 = ModuleShape("train_8192to28672_r384_t8192", 28672, 8192, 384, 8192,
 
 
 def _normal(gen, shape, std, dtype):
-    return (torch.randn(*shape, generator=gen, dtype=torch.float32) * std).to(dtype)
+    return (torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device) *
+            std).to(dtype)
 
 
 def draw_weights(gen, d_out, d_in, r, dtype, sigma_B, sigma_m):
@@ -62,7 +63,7 @@ def draw_weights(gen, d_out, d_in, r, dtype, sigma_B, sigma_m):
     W = _normal(gen, (d_out, d_in), d_in ** -0.5, dtype)
     A = _normal(gen, (r, d_in), d_in ** -0.5, dtype)
     B = _normal(gen, (d_out, r), sigma_B, dtype)
-    z = torch.randn(d_out, generator=gen, dtype=torch.float32).double()
+    z = torch.randn(d_out, generator=gen, dtype=torch.float32, device=gen.device).double()
     row = torch.linalg.vector_norm(W.double(), dim=1)
     m = (row * (1.0 + sigma_m * z)).float()
     return W, A, B, m
@@ -118,3 +119,26 @@ def sample_indices(seed, n, *bounds):
     out = torch.stack(cols, dim=1)
     edges = torch.tensor([[0] * len(bounds), [b - 1 for b in bounds]])
     return torch.cat([edges, out], dim=0).tolist()
+
+
+# The seven adapted projections of one decoder layer as (name, d_out, d_in):
+# query, key, value, output, gate, up, down.  Default widths are those of an
+# 8B-class decoder with grouped-query attention (hidden 4096, key/value 1024,
+# MLP 14336), the scale of the smallest models the Scaling-DoRA abstract
+# measures.
+def decoder_layer_shapes(hidden=4096, kv=1024, inter=14336):
+    return [("q", hidden, hidden), ("k", kv, hidden), ("v", kv, hidden), ("o", hidden, hidden),
+            ("gate", inter, hidden), ("up", inter, hidden), ("down", hidden, inter)]
+
+
+def make_group(shapes, r, dtype="bf16", s=1.0, sigma_B=0.02, sigma_m=0.01, seed=0,
+               device="cpu"):
+    """Modules of the given (name, d_out, d_in) shapes from one generator on
+    `device`, in list order; each a dict with W, A, B, m, s, name."""
+    dt = _DT[dtype]
+    gen = torch.Generator(device).manual_seed(seed)
+    out = []
+    for name, d_out, d_in in shapes:
+        W, A, B, m = draw_weights(gen, d_out, d_in, r, dt, sigma_B, sigma_m)
+        out.append({"W": W, "A": A, "B": B, "m": m, "s": float(s), "name": name})
+    return out

@@ -202,6 +202,59 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
                                float *dm, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Grouped calls - many adapted modules in few launches.  The "Scaling DoRA"
+ * abstract motivates the factored norm with models that carry hundreds of
+ * adapted modules; these calls give each kernel of the norm (and of the
+ * forward of sibling modules that share one input, such as the query, key
+ * and value projections) one launch per 16 modules instead of one per
+ * module, with every module's products sharing the GPU at once.
+ *
+ * dora_module describes one module: W [d_out, d_in], A [r, d_in],
+ * B [d_out, r] in `dtype`, m [d_out] fp32 (not read by the norm), scale s.
+ * The array is read on the host during the call only.
+ */
+typedef struct dora_module {
+    const void *W;
+    const void *A;
+    const void *B;
+    const float *m;
+    float s;
+    int64_t d_out, d_in, r;
+} dora_module;
+
+/*
+ * dora_factored_norm_grouped - n[i] = the row norms of W_i + s_i B_i A_i for
+ * every module, as dora_factored_norm computes them (the same terms and
+ * precision; the split-K plan may differ, so bits may too).  n is a host
+ * array of `count` device pointers ([d_out_i] fp32 each), pairwise disjoint
+ * and disjoint from every module's W, A, B and the workspace.  fp32 modules
+ * (and bf16 ones whose operands reach 2 GiB) run module by module.
+ *   ws: dora_factored_norm_grouped_workspace(mods, count, dtype) bytes.
+ */
+size_t dora_factored_norm_grouped_workspace(const dora_module *mods, int count, int dtype);
+int dora_factored_norm_grouped(const dora_module *mods, int count, int dtype, float *const *n,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dora_forward_grouped - dora_forward for `count` modules on the same input
+ * x [T, d_in] (every module's d_in must equal d_in): y[i] [T, d_out_i],
+ * n_out[i] [d_out_i] fp32, optional P_out[i] [T, r_i] (P_out itself may be
+ * NULL), optional cached norms n_in[i] (n_in itself may be NULL; a given
+ * n_in[i] skips that module's norm and may equal n_out[i]).  Host arrays of
+ * device pointers; every output is disjoint from every input and from every
+ * other output.  Per 16 modules: one launch of all x A_i^T, one of the s P
+ * scalings, one of the fused products with the magnitude epilogue.
+ *   ws: dora_forward_grouped_workspace(mods, count, T, dtype, n_in, P_out)
+ *   bytes (it depends on which norms are cached and which P are kept).
+ */
+size_t dora_forward_grouped_workspace(const dora_module *mods, int count, int64_t T, int dtype,
+                                      const float *const *n_in, void *const *P_out);
+int dora_forward_grouped(const void *x, int64_t T, int64_t d_in, const dora_module *mods,
+                         int count, int dtype, void *const *y, float *const *n_out,
+                         void *const *P_out, const float *const *n_in, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/*
  * dora_merge - the merged weight W' = g (.) (W + s B A), g = m / n by rows,
  * for inference: the DoRA summary pages ("Method"; Key Points 3 and 5) note
  * that the adapted weight folds into the base weight, so inference is a

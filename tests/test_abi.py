@@ -231,3 +231,96 @@ def test_merge_workspace_has_no_dense_term():
     for d_out, d_in in ((8192, 8192), (28672, 8192), (8192, 262144)):
         ws = L.dora_merge_workspace(d_out, d_in, 384, BF16)
         assert 0 < ws <= L.dora_norm_workspace(d_out, d_in, 384, BF16) + d_out * 4 + 256
+
+
+def _mods(shapes, base=FAKE):
+    """Module descriptors with fake, disjoint, aligned addresses."""
+    arr = (D.DoraModule * max(len(shapes), 1))()
+    for k, (d_out, d_in, r) in enumerate(shapes):
+        a = base + (k << 36)
+        arr[k] = D.DoraModule(a, a + (1 << 34), a + (2 << 34), a + (3 << 34), 1.0, d_out, d_in, r)
+    return arr
+
+
+def _vp(addrs):
+    arr = (ctypes.c_void_p * max(len(addrs), 1))(*addrs)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_grouped_norm_validation():
+    L = D.lib()
+    shapes = [(64, 128, 8), (264, 520, 24), (128, 128, 16)]
+    mods = _mods(shapes)
+    need = L.dora_factored_norm_grouped_workspace(mods, 3, BF16)
+    assert need > 0
+    outs = [FAKE + (60 << 36) + (k << 20) for k in range(3)]
+    n, keep = _vp(outs)
+    ws = FAKE + (61 << 36)
+
+    def call(m=mods, count=3, nn=n, w=ws, wb=need, dt=BF16):
+        return L.dora_factored_norm_grouped(m, count, dt, nn, _p(w), wb, None)
+
+    assert call(count=0) == OK                       # nothing to do, nothing launched
+    assert call(count=-1) == E_SHAPE
+    assert call(m=None) == E_NULL
+    assert call(nn=None) == E_NULL
+    assert call(wb=need - 1) == E_WS
+    assert call(dt=5) == E_DTYPE
+    bad = _mods([(64, 128, 8), (264, 520, 24), (128, 100, 16)])  # module 2: d_in % 8
+    assert call(m=bad) == E_SHAPE
+    assert b"module 2" in L.dora_last_error()
+    same, keep2 = _vp([outs[0], outs[0] + 64, outs[2]])         # n[0] and n[1] overlap
+    assert call(nn=same) == E_ALIAS
+    into_w, keep3 = _vp([outs[0], FAKE + (1 << 36) + 256, outs[2]])  # n[1] inside W of module 1
+    assert call(nn=into_w) == E_ALIAS
+    assert call(w=FAKE + 4096) == E_ALIAS            # workspace inside module 0's W
+
+
+def test_grouped_workspaces_have_no_dense_term():
+    """The grouped norm keeps per-module O(d_out + r^2) partials only, and
+    the chunks of 16 reuse one region: a model's worth of modules needs no
+    more than one chunk's partials."""
+    L = D.lib()
+    r = 384
+    layer = [(4096, 4096, r), (1024, 4096, r), (1024, 4096, r), (4096, 4096, r),
+             (14336, 4096, r), (14336, 4096, r), (4096, 14336, r)]
+    one = L.dora_factored_norm_grouped_workspace(_mods(layer), 7, BF16)
+    many = L.dora_factored_norm_grouped_workspace(_mods(layer * 32), 224, BF16)
+    assert 0 < one <= many
+    assert many <= 16 * (33 * r * r * 4 + 2 * r * r * 2 + 33 * 2 * 14336 * 4) + 16 * 5 * 256
+    # no d_in term: the same modules with 16x wider inputs change split counts only
+    wide = L.dora_factored_norm_grouped_workspace(
+        _mods([(d_out, 16 * d_in, r) for d_out, d_in, _ in layer]), 7, BF16)
+    assert wide <= 16 * (33 * r * r * 4 + 2 * r * r * 2 + 33 * 2 * 14336 * 4) + 16 * 5 * 256
+
+
+def test_grouped_forward_validation():
+    L = D.lib()
+    T, d_in = 16, 128
+    shapes = [(64, d_in, 8), (128, d_in, 16)]
+    mods = _mods(shapes)
+    need = L.dora_forward_grouped_workspace(mods, 2, T, BF16, None, None)
+    assert need > 0
+    x = FAKE + (50 << 36)
+    ys, k1 = _vp([FAKE + (51 << 36), FAKE + (51 << 36) + (1 << 24)])
+    ns, k2 = _vp([FAKE + (52 << 36), FAKE + (52 << 36) + (1 << 20)])
+    ws = FAKE + (53 << 36)
+
+    def call(m=mods, count=2, xx=x, dinn=d_in, y=ys, n=ns, P=None, nin=None, wb=need, TT=T):
+        return L.dora_forward_grouped(_p(xx), TT, dinn, m, count, BF16, y, n, P, nin, _p(ws), wb,
+                                      None)
+
+    assert call(count=0) == OK
+    assert call(dinn=256) == E_SHAPE                 # modules' d_in differ from x's
+    assert b"module 0" in L.dora_last_error()
+    assert call(xx=0) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(wb=need - 1) == E_WS
+    assert call(TT=-2) == E_SHAPE
+    clash, k3 = _vp([FAKE + (51 << 36), FAKE + (51 << 36) + 64])  # y[0] and y[1] overlap
+    assert call(y=clash) == E_ALIAS
+    over_x, k4 = _vp([x, FAKE + (51 << 36) + (1 << 24)])       # y[0] over x
+    assert call(y=over_x) == E_ALIAS
+    # a cached norm changes the workspace (that module's norm partials are not needed)
+    cached, k5 = _vp([FAKE + (54 << 36), 0])
+    assert L.dora_forward_grouped_workspace(mods, 2, T, BF16, cached, None) <= need
