@@ -419,31 +419,29 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.f;
     // ROWSQ: sums of squares of A's rows from the A fragments already in
-    // registers (every wave holds all BM rows); wave wn takes the 32-row
-    // blocks i = wn, wn + WN, ..., lane l row i * 32 + (l & 31), K half l >> 5.
-    constexpr int NSQ = (TM + WN - 1) / WN;
-    float sq[NSQ];
+    // registers (every wave holds all BM rows): lane l covers row
+    // i * 32 + (l & 31) of block i and K half l >> 5 of each 16-wide step.
+    // Every wave sums every block (branch-free, two v_dot2_f32_bf16 chains
+    // per block, spread over the first MFMAs of a half) and keeps blocks
+    // i = wn, wn + WN, ... at the end.
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    float sq[ROWSQ ? TM : 1][2];
 #pragma unroll
-    for (int u = 0; u < NSQ; ++u)
-        sq[u] = 0.f;
-    auto rowsq_half = [&](const Frags<TM, TN> &f) {
-        if (tn == 0) {
-            // fragment indices stay compile-time constants (a register array
-            // indexed by the wave number would be placed in scratch)
+    for (int i = 0; i < (ROWSQ ? TM : 1); ++i)
+        sq[i][0] = sq[i][1] = 0.f;
+    auto rowsq_part = [&](const Frags<TM, TN> &f, auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i % WN == wn) {
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const bf16x8_t v = f.a[kk][i];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const float x = static_cast<float>(v[q]);
-                            sq[i / WN] = __fmaf_rn(x, x, sq[i / WN]);
-                        }
-                    }
-                }
-            }
+        for (int i = 0; i < TM; ++i) {
+            const bf16x8_t v = f.a[kk][i];
+            const bf16x2_t p0 = __builtin_shufflevector(v, v, 0, 1);
+            const bf16x2_t p1 = __builtin_shufflevector(v, v, 2, 3);
+            const bf16x2_t p2 = __builtin_shufflevector(v, v, 4, 5);
+            const bf16x2_t p3 = __builtin_shufflevector(v, v, 6, 7);
+            sq[i][0] = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, sq[i][0], false);
+            sq[i][1] = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, sq[i][1], false);
+            sq[i][0] = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, sq[i][0], false);
+            sq[i][1] = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, sq[i][1], false);
         }
     };
 
@@ -472,11 +470,20 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         // half 0 reads half 1 of the same stage; half 1 reads half 0 of D + 1
         const unsigned char *An = slot(H == 0 ? D : D + 1);
         const unsigned char *Bn = An + C::A_BYTES;
+        // the reads and loads are spread over the first SPAN MFMAs: the last
+        // read then has TAIL MFMAs of time to land before the next half
+        // waits for it (measured: worth it for the 1 x 4 wave layout)
+        constexpr int TAIL = WM == 1 ? 8 : 0;
+        constexpr int SPAN = NMF - TAIL;
+        static_assert(SPAN >= 2, "MFMA slots");
         static_for<NMF>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
             mfma_one<TM, TN, q>(acc, cur);
-            static_for<(q + 1) * NOPS / NMF - q * NOPS / NMF>([&](auto oc) {
-                constexpr int o = q * NOPS / NMF + decltype(oc)::value;
+            if constexpr (ROWSQ && q < 2)
+                rowsq_part(cur, std::integral_constant<int, q>{});
+            constexpr int cnt = q < SPAN ? (q + 1) * NOPS / SPAN - q * NOPS / SPAN : 0;
+            static_for<cnt>([&](auto oc) {
+                constexpr int o = q * NOPS / SPAN + decltype(oc)::value;
                 // load groups spread evenly, from the first slot on (they
                 // have a deadline; the reads only feed the next half)
                 constexpr int grp = (o * NGH) % NOPS < NGH ? (o * NGH) / NOPS : -1;
@@ -489,8 +496,6 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             });
             __builtin_amdgcn_sched_barrier(0);
         });
-        if constexpr (ROWSQ)
-            rowsq_half(cur);
     };
 
     FR fa, fb;  // half 0 and half 1 of a stage
@@ -520,9 +525,14 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     if constexpr (ROWSQ) {
         if (g.rowsq != nullptr && tn == 0) {
 #pragma unroll
-            for (int u = 0; u < NSQ; ++u) {
+            for (int u = 0; u < (TM + WN - 1) / WN; ++u) {
                 const int i = wn + u * WN;
-                const float t = sq[u] + __shfl_xor(sq[u], 32);
+                float su = 0.f;
+#pragma unroll
+                for (int b = 0; b < TM; ++b)
+                    if (b == i)
+                        su = sq[b][0] + sq[b][1];
+                const float t = su + __shfl_xor(su, 32);
                 const int64_t row = m0 + i * 32 + lane;
                 if (i < TM && lane < 32 && row < g.M)
                     g.rowsq[static_cast<int64_t>(z) * g.M + row] = t;
