@@ -787,10 +787,21 @@ NormChunk plan_norm_chunk(const dora_module *mods, int i0, int i1, int dtype)
     return c;
 }
 
+// Longest first: modules in order of decreasing d_in (the K of their
+// largest product), so that each chunk holds products of similar length
+// and a launch's long tiles start first.
+std::vector<int> by_length(const dora_module *mods, std::vector<int> which)
+{
+    std::stable_sort(which.begin(), which.end(),
+                     [&](int a, int b) { return mods[a].d_in > mods[b].d_in; });
+    return which;
+}
+
 std::vector<NormChunk> plan_norm_group(const dora_module *mods, const std::vector<int> &which,
                                        int dtype, size_t &bytes)
 {
-    // `which` lists the modules to normalise; chunks are runs of it
+    // `which` lists the modules to normalise (in chunk order); chunks are
+    // runs of it
     std::vector<dora_module> sel;
     for (int i : which)
         sel.push_back(mods[i]);
@@ -915,6 +926,7 @@ FwdGroupPlan plan_forward_group(const dora_module *mods, int count, int64_t T, i
     for (int i = 0; i < count; ++i)
         if (!n_in || !n_in[i])
             f.need_norm.push_back(i);
+    f.need_norm = by_length(mods, f.need_norm);
     f.norm = plan_norm_group(mods, f.need_norm, dtype, f.norm_bytes);
     const size_t e = esize(dtype);
     size_t most = 0;
@@ -1339,6 +1351,7 @@ size_t dora_factored_norm_grouped_workspace(const dora_module *mods, int count, 
     std::vector<int> all(count);
     for (int i = 0; i < count; ++i)
         all[i] = i;
+    all = by_length(mods, all);
     size_t bytes = 0;
     plan_norm_group(mods, all, dtype, bytes);
     return bytes;
@@ -1357,6 +1370,7 @@ int dora_factored_norm_grouped(const dora_module *mods, int count, int dtype, fl
     std::vector<int> all(count);
     for (int i = 0; i < count; ++i)
         all[i] = i;
+    all = by_length(mods, all);
     size_t bytes = 0;
     const std::vector<NormChunk> chunks = plan_norm_group(mods, all, dtype, bytes);
     DORA_CHECK(check_ws(ws, ws_bytes, bytes));
