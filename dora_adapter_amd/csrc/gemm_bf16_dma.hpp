@@ -195,6 +195,9 @@ __device__ __forceinline__ void lds_dma16x4(__amdgpu_buffer_rsrc_t rsrc, uint32_
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor range
 
+// Load modes of a stage (see dma_group).
+constexpr int LOAD_ANY = 0, LOAD_SEG0 = 1, LOAD_SEG1 = 2;
+
 // One operand's load plan: per-lane byte offsets (biased, see GROUP_BIAS)
 // of the sources of the wave's load instructions, computed once per tile.
 // Wave w fills the PER consecutive 1 KiB blocks from w * PER.
@@ -364,9 +367,16 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     // nothing and deposit zeros in a slot no later stage reads, so every
     // stage has the same shape (no branches, the same vmcnt bookkeeping).
     constexpr int GA = DA::PER / GROUP, NG = C::LPS / GROUP;
-    auto dma_group = [&](int64_t sd, int d) {
+    //
+    // MODE (compile-time at each call site) removes the per-lane selects
+    // from the common stages: LOAD_SEG0 / LOAD_SEG1 for stages lying wholly
+    // inside K of segment 0 / 1 (or past the end, where the empty range makes
+    // the offsets irrelevant); LOAD_ANY decides per lane (a segment's tail
+    // stage, whose chunks past K must load as zeros).
+    auto dma_group = [&](int64_t sd, int d, auto mode_c) {
+        constexpr int MODE = decltype(mode_c)::value;
         const bool live = sd < s_end;
-        const bool sg1 = sd >= st1;
+        const bool sg1 = MODE == LOAD_ANY ? sd >= st1 : MODE == LOAD_SEG1;
         const int64_t kd = (sg1 ? sd - st1 : sd) * BK;
         const int64_t kseg = sg1 ? g.seg[1].K : g.seg[0].K;
         const bool isa = d < GA;
@@ -386,7 +396,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 const uint32_t off = sg1 ? da1.off[i0 + j] : da0.off[i0 + j];
                 if constexpr (AK) {
                     const uint32_t kq = sg1 ? da1.kch[i0 + j] : da0.kch[i0 + j];
-                    v[j] = kd + kq < kseg ? off : OOB_OFFSET;
+                    v[j] = (MODE != LOAD_ANY || kd + kq < kseg) ? off : OOB_OFFSET;
                 } else {
                     v[j] = off + static_cast<uint32_t>(kd * ld * 2);
                 }
@@ -400,7 +410,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 const uint32_t off = sg1 ? db1.off[i0 + j] : db0.off[i0 + j];
                 if constexpr (BKM) {
                     const uint32_t kq = sg1 ? db1.kch[i0 + j] : db0.kch[i0 + j];
-                    v[j] = kd + kq < kseg ? off : OOB_OFFSET;
+                    v[j] = (MODE != LOAD_ANY || kd + kq < kseg) ? off : OOB_OFFSET;
                 } else {
                     v[j] = off + static_cast<uint32_t>(kd * ld * 2);
                 }
@@ -453,7 +463,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     constexpr int NMF = 2 * TM * TN;    // MFMAs per half
     constexpr int NRD = 2 * (TM + TN);  // fragment reads per half
     using FR = Frags<TM, TN>;
-    auto half = [&](auto h_c, int64_t D, FR &cur, FR &nxt) {
+    auto half = [&](auto h_c, int64_t D, FR &cur, FR &nxt, auto mode_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr int NGH = H == 1 ? NG : 0;  // load groups in this half
         constexpr int NOPS = NRD + NGH;
@@ -489,7 +499,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 constexpr int grp = (o * NGH) % NOPS < NGH ? (o * NGH) / NOPS : -1;
                 constexpr int rd = o - (o * NGH + NOPS - 1) / NOPS;
                 if constexpr (NGH > 0 && grp >= 0)
-                    dma_group(D + 2, grp);
+                    dma_group(D + 2, grp, mode_c);
                 else
                     read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, rd>(nxt, An, Bn, 1 - H, wm, wn,
                                                                     lane);
@@ -506,7 +516,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         for (int p = 0; p < 2; ++p)
 #pragma unroll
             for (int d = 0; d < NG; ++d)
-                dma_group(s_begin + p, d);
+                dma_group(s_begin + p, d, std::integral_constant<int, LOAD_ANY>{});
         wait_vmcnt<C::LPS>();  // stage s_begin has landed
         stage_barrier();
         static_for<NRD>([&](auto oc) {
@@ -514,10 +524,27 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 fa, slot(s_begin), slot(s_begin) + C::A_BYTES, 0, wm, wn, lane);
         });
         // the last stage still reads a (stale) next slot; nothing uses it
-        for (int64_t D = s_begin; D < s_end; ++D) {
-            half(std::integral_constant<int, 0>{}, D, fa, fb);
-            half(std::integral_constant<int, 1>{}, D, fb, fa);
-        }
+        // Stage D's half 1 loads stage L = D + 2.  The stages run as four
+        // loops, each with one load mode: L inside segment 0's whole stages,
+        // then up to segment 1 (segment 0's tail stage), L inside segment 1's
+        // whole stages, then the rest (segment 1's tail, loads past the end).
+        auto stages = [&](int64_t D0, int64_t D1, auto mode_c) {
+            for (int64_t D = D0; D < D1; ++D) {
+                half(std::integral_constant<int, 0>{}, D, fa, fb,
+                     std::integral_constant<int, LOAD_ANY>{});
+                half(std::integral_constant<int, 1>{}, D, fb, fa, mode_c);
+            }
+        };
+        auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); };
+        const int64_t full0 = g.seg[0].K / BK;
+        const int64_t full1 = g.nseg > 1 ? g.seg[1].K / BK : 0;
+        const int64_t e0 = clamp(full0 - 2, s_begin, s_end);
+        const int64_t b1 = clamp(st1 - 2, e0, s_end);
+        const int64_t e1 = clamp(st1 + full1 - 2, b1, s_end);
+        stages(s_begin, e0, std::integral_constant<int, LOAD_SEG0>{});
+        stages(e0, b1, std::integral_constant<int, LOAD_ANY>{});
+        stages(b1, e1, std::integral_constant<int, LOAD_SEG1>{});
+        stages(e1, s_end, std::integral_constant<int, LOAD_ANY>{});
         wait_vmcnt<0>();  // the empty loads past the end have deposited their zeros
     }
     stage_barrier();  // every wave is done reading the slots before LDS is reused

@@ -31,6 +31,7 @@ def _fwd_bwd(mod):
     (300, 264, 520, 24, "bf16", 1.0),
     (777, 1000, 1024, 40, "bf16", 2.0),
     (513, 384, 768, 128, "bf16", 0.5),
+    (64, 4000, 1024, 40, "bf16", 1.0),  # dx: split-K over [dh | Q], ragged tails in both
 ])
 def test_backward_full(T, d_out, d_in, r, dtype, s):
     say("backward", T, d_out, d_in, r, dtype)

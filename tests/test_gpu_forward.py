@@ -40,6 +40,7 @@ def test_tiny_fp32_module():
     (777, 1000, 1024, 40, 2.0),
     (1, 512, 384, 384, 1.0),
     (513, 384, 2048, 128, 0.5),
+    (64, 512, 4008, 40, 1.0),  # few tiles: split-K across both K segments, ragged tails
 ])
 def test_bf16_matches_oracle(T, d_out, d_in, r, s):
     say("forward bf16", T, d_out, d_in, r)
