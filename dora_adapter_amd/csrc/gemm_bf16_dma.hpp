@@ -196,7 +196,7 @@ __device__ __forceinline__ void lds_dma16x4(__amdgpu_buffer_rsrc_t rsrc, uint32_
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor range
 
 // Load modes of a stage (see dma_group).
-constexpr int LOAD_ANY = 0, LOAD_SEG0 = 1, LOAD_SEG1 = 2;
+constexpr int LOAD_ANY = 0, LOAD_SEG0 = 1, LOAD_SEG1 = 2, LOAD_NONE = 3;
 
 // One operand's load plan: per-lane byte offsets (biased, see GROUP_BIAS)
 // of the sources of the wave's load instructions, computed once per tile.
@@ -369,13 +369,16 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     constexpr int GA = DA::PER / GROUP, NG = C::LPS / GROUP;
     //
     // MODE (compile-time at each call site) removes the per-lane selects
-    // from the common stages: LOAD_SEG0 / LOAD_SEG1 for stages lying wholly
-    // inside K of segment 0 / 1 (or past the end, where the empty range makes
-    // the offsets irrelevant); LOAD_ANY decides per lane (a segment's tail
-    // stage, whose chunks past K must load as zeros).
+    // from the common stages: LOAD_SEG0 / LOAD_SEG1 for live stages lying
+    // wholly inside K of segment 0 / 1, LOAD_NONE for stages past the
+    // split's end (no loads), LOAD_ANY decides per lane (a segment's tail
+    // stage, whose chunks past K must load as zeros; any stage of the
+    // prologue).
     auto dma_group = [&](int64_t sd, int d, auto mode_c) {
         constexpr int MODE = decltype(mode_c)::value;
-        const bool live = sd < s_end;
+        if constexpr (MODE == LOAD_NONE)
+            return;  // a stage past this split's end: nothing reads its slot
+        const bool live = MODE == LOAD_ANY ? sd < s_end : true;
         const bool sg1 = MODE == LOAD_ANY ? sd >= st1 : MODE == LOAD_SEG1;
         const int64_t kd = (sg1 ? sd - st1 : sd) * BK;
         const int64_t kseg = sg1 ? g.seg[1].K : g.seg[0].K;
@@ -524,10 +527,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 fa, slot(s_begin), slot(s_begin) + C::A_BYTES, 0, wm, wn, lane);
         });
         // the last stage still reads a (stale) next slot; nothing uses it
-        // Stage D's half 1 loads stage L = D + 2.  The stages run as four
+        // Stage D's half 1 loads stage L = D + 2.  The stages run as five
         // loops, each with one load mode: L inside segment 0's whole stages,
-        // then up to segment 1 (segment 0's tail stage), L inside segment 1's
-        // whole stages, then the rest (segment 1's tail, loads past the end).
+        // segment 0's tail stage, L inside segment 1's whole stages, segment
+        // 1's tail stage, and L past this split's end (the last two stages).
         auto stages = [&](int64_t D0, int64_t D1, auto mode_c) {
             for (int64_t D = D0; D < D1; ++D) {
                 half(std::integral_constant<int, 0>{}, D, fa, fb,
@@ -536,15 +539,18 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             }
         };
         auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); };
+        auto lesser = [](int64_t a, int64_t b) { return a < b ? a : b; };
         const int64_t full0 = g.seg[0].K / BK;
         const int64_t full1 = g.nseg > 1 ? g.seg[1].K / BK : 0;
-        const int64_t e0 = clamp(full0 - 2, s_begin, s_end);
-        const int64_t b1 = clamp(st1 - 2, e0, s_end);
-        const int64_t e1 = clamp(st1 + full1 - 2, b1, s_end);
+        const int64_t e0 = clamp(lesser(full0, s_end) - 2, s_begin, s_end);
+        const int64_t b1 = clamp(lesser(st1, s_end) - 2, e0, s_end);
+        const int64_t e1 = clamp(lesser(st1 + full1, s_end) - 2, b1, s_end);
+        const int64_t dd = clamp(s_end - 2, e1, s_end);
         stages(s_begin, e0, std::integral_constant<int, LOAD_SEG0>{});
         stages(e0, b1, std::integral_constant<int, LOAD_ANY>{});
         stages(b1, e1, std::integral_constant<int, LOAD_SEG1>{});
-        stages(e1, s_end, std::integral_constant<int, LOAD_ANY>{});
+        stages(e1, dd, std::integral_constant<int, LOAD_ANY>{});
+        stages(dd, s_end, std::integral_constant<int, LOAD_NONE>{});
         wait_vmcnt<0>();  // the empty loads past the end have deposited their zeros
     }
     stage_barrier();  // every wave is done reading the slots before LDS is reused
