@@ -46,7 +46,7 @@ METRIC = "DoRA module fwd µs + compose HBM GB/s + norm-GEMM MFMA util, r=384 bf
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "base_gemm_traffic.json")
-KERNEL_WARMUP = 3  # untimed launches before each kernel-leg burst
+KERNEL_WARMUP = 10  # untimed launches before each kernel-leg burst (the clock settles)
 GROUP_LAYERS = 8   # decoder layers whose 7 projections form the grouped-norm workload
 
 
