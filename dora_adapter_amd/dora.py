@@ -47,7 +47,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} not built; run __graft_entry__.build() first")
+            raise ImportError(f"{LIB_PATH} not built; run python -m dora_adapter_amd.build first")
         L = ctypes.CDLL(LIB_PATH)
         p, i64, sz, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         c_int = ctypes.c_int
