@@ -315,42 +315,84 @@ __global__ void gram_finalize_grouped_kernel(ItemGroup<GramItem> g, int bf16)
 }
 
 // Backward through the norm: cs_i = -s m_i dm_i / n_i^2 (the row
-// coefficient of the norm's gradient, times -s) and cB = cs (.) B.
-template <typename T>
+// coefficient of the norm's gradient, times -s) and cB = cs (.) B.  VEC: a
+// thread takes 8 consecutive elements of a row (r a multiple of 8).
+template <typename T, bool VEC>
 __global__ void norm_grad_coef_kernel(const float *__restrict__ m, const float *__restrict__ dm,
                                       const float *__restrict__ n, float s,
                                       const T *__restrict__ B, int64_t d_out, int64_t r,
                                       float *__restrict__ cs, T *__restrict__ cB)
 {
-    const int64_t total = d_out * r;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t i = e / r;
+    const int64_t per = VEC ? r / 8 : r;  // work items per row
+    const int64_t total = d_out * per;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < total;
+         q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t i = q / per;
         const float c = -s * m[i] * dm[i] / (n[i] * n[i]);
-        if (e % r == 0)
+        if (q % per == 0)
             cs[i] = c;
-        Vec8<T>::store1(cB + e, c * Vec8<T>::load1(B + e));
+        if (VEC) {
+            const int64_t e = q * 8;
+            float v[8];
+            Vec8<T>::load(B + e, v);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = c * v[k];
+            Vec8<T>::store(cB + e, v);
+        } else {
+            Vec8<T>::store1(cB + q, c * Vec8<T>::load1(B + q));
+        }
     }
 }
 
 // out[i, j] = sum_z part[z][i, j] + f_i sum_u ypart[u][i, j] (f_i = rowscale[i],
-// or 1), in this fixed order, rounded once.
-template <typename T>
+// or 1), in this fixed order, rounded once.  VEC: 8 consecutive elements of
+// a row per thread (N a multiple of 8).
+template <typename T, bool VEC>
 __global__ void combine_rows_kernel(const float *__restrict__ part, int np,
                                     const float *__restrict__ ypart, int ny,
                                     const float *__restrict__ rowscale, int64_t M, int64_t N,
                                     T *__restrict__ out)
 {
     const int64_t MN = M * N;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < MN;
-         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        float a = 0.f, y = 0.f;
-        for (int z = 0; z < np; ++z)
-            a += part[static_cast<int64_t>(z) * MN + e];
-        for (int u = 0; u < ny; ++u)
-            y += ypart[static_cast<int64_t>(u) * MN + e];
+    constexpr int L = VEC ? 8 : 1;
+    const int64_t items = MN / L;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < items;
+         q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t e = q * L;
+        float a[L], y[L], t[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k)
+            a[k] = y[k] = 0.f;
+        for (int z = 0; z < np; ++z) {
+            if constexpr (VEC) {
+                Vec8<float>::load(part + static_cast<int64_t>(z) * MN + e, t);
+            } else {
+                t[0] = part[static_cast<int64_t>(z) * MN + e];
+            }
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+                a[k] += t[k];
+        }
+        for (int u = 0; u < ny; ++u) {
+            if constexpr (VEC) {
+                Vec8<float>::load(ypart + static_cast<int64_t>(u) * MN + e, t);
+            } else {
+                t[0] = ypart[static_cast<int64_t>(u) * MN + e];
+            }
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+                y[k] += t[k];
+        }
         const float f = rowscale != nullptr ? rowscale[e / N] : 1.f;
-        Vec8<T>::store1(out + e, __fmaf_rn(f, y, a));
+#pragma unroll
+        for (int k = 0; k < L; ++k)
+            t[k] = __fmaf_rn(f, y[k], a[k]);
+        if constexpr (VEC) {
+            Vec8<T>::store(out + e, t);
+        } else {
+            Vec8<T>::store1(out + e, t[0]);
+        }
     }
 }
 
@@ -574,17 +616,30 @@ hipError_t launch_norm_grad_coef(int bf16, const float *m, const float *dm, cons
 {
     if (d_out == 0)
         return hipSuccess;
-    int64_t blocks = (d_out * r + EW_THREADS - 1) / EW_THREADS;
+    const bool vec = r % 8 == 0;
+    int64_t blocks = (d_out * (vec ? r / 8 : r) + EW_THREADS - 1) / EW_THREADS;
     if (blocks > 8192)
         blocks = 8192;
     const dim3 grid(static_cast<unsigned>(blocks));
-    if (bf16)
-        hipLaunchKernelGGL(norm_grad_coef_kernel<uint16_t>, grid, dim3(EW_THREADS), 0, st, m, dm, n,
-                           s, static_cast<const uint16_t *>(B), d_out, r, cs,
-                           static_cast<uint16_t *>(cB));
-    else
-        hipLaunchKernelGGL(norm_grad_coef_kernel<float>, grid, dim3(EW_THREADS), 0, st, m, dm, n, s,
-                           static_cast<const float *>(B), d_out, r, cs, static_cast<float *>(cB));
+    if (bf16) {
+        auto *b = static_cast<const uint16_t *>(B);
+        auto *o = static_cast<uint16_t *>(cB);
+        if (vec)
+            hipLaunchKernelGGL((norm_grad_coef_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0,
+                               st, m, dm, n, s, b, d_out, r, cs, o);
+        else
+            hipLaunchKernelGGL((norm_grad_coef_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0,
+                               st, m, dm, n, s, b, d_out, r, cs, o);
+    } else {
+        auto *b = static_cast<const float *>(B);
+        auto *o = static_cast<float *>(cB);
+        if (vec)
+            hipLaunchKernelGGL((norm_grad_coef_kernel<float, true>), grid, dim3(EW_THREADS), 0, st,
+                               m, dm, n, s, b, d_out, r, cs, o);
+        else
+            hipLaunchKernelGGL((norm_grad_coef_kernel<float, false>), grid, dim3(EW_THREADS), 0, st,
+                               m, dm, n, s, b, d_out, r, cs, o);
+    }
     return hipGetLastError();
 }
 
@@ -594,16 +649,28 @@ hipError_t launch_combine_rows(int bf16, const float *part, int np, const float 
 {
     if (M == 0 || N == 0)
         return hipSuccess;
-    int64_t blocks = (M * N + EW_THREADS - 1) / EW_THREADS;
+    const bool vec = N % 8 == 0;
+    int64_t blocks = (M * N / (vec ? 8 : 1) + EW_THREADS - 1) / EW_THREADS;
     if (blocks > 8192)
         blocks = 8192;
     const dim3 grid(static_cast<unsigned>(blocks));
-    if (bf16)
-        hipLaunchKernelGGL(combine_rows_kernel<uint16_t>, grid, dim3(EW_THREADS), 0, st, part, np,
-                           ypart, ny, rowscale, M, N, static_cast<uint16_t *>(out));
-    else
-        hipLaunchKernelGGL(combine_rows_kernel<float>, grid, dim3(EW_THREADS), 0, st, part, np,
-                           ypart, ny, rowscale, M, N, static_cast<float *>(out));
+    if (bf16) {
+        auto *o = static_cast<uint16_t *>(out);
+        if (vec)
+            hipLaunchKernelGGL((combine_rows_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0, st,
+                               part, np, ypart, ny, rowscale, M, N, o);
+        else
+            hipLaunchKernelGGL((combine_rows_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0,
+                               st, part, np, ypart, ny, rowscale, M, N, o);
+    } else {
+        auto *o = static_cast<float *>(out);
+        if (vec)
+            hipLaunchKernelGGL((combine_rows_kernel<float, true>), grid, dim3(EW_THREADS), 0, st,
+                               part, np, ypart, ny, rowscale, M, N, o);
+        else
+            hipLaunchKernelGGL((combine_rows_kernel<float, false>), grid, dim3(EW_THREADS), 0, st,
+                               part, np, ypart, ny, rowscale, M, N, o);
+    }
     return hipGetLastError();
 }
 
