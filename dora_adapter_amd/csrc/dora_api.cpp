@@ -233,6 +233,23 @@ MergePlan plan_merge(int64_t d_out, int64_t d_in, int64_t r, int dtype)
     const GemmShape sh{d_out, d_in, {r, 0}, 1, 1,
                        dma_operand(d_out, r) && dma_mn_operand(r, d_in)};
     p.g = plan_gemm(bf, sh, kNoSplit);
+    if (bf && sh.dma_ok) {
+        // The product is short (K = r) and its epilogue streams W in and W'
+        // out: 128 x 128 tiles keep two workgroups per CU, so one's epilogue
+        // traffic overlaps the other's MFMAs (measured faster than the
+        // compute-only time model's pick at 28672 x 8192, r 384).
+        for (int c = 0; c < gemm_bf16_num_cfgs(); ++c) {
+            const TileCfg t = gemm_bf16_cfg(c);
+            if (t.dma && t.store_ok && t.BM == 128 && t.BN == 128) {
+                p.g.cfg = c;
+                p.g.BM = t.BM;
+                p.g.BN = t.BN;
+                p.g.splits = 1;
+                p.g.sps = (r + t.bk - 1) / t.bk;
+                p.g.ntn = static_cast<int>((d_in + t.BN - 1) / t.BN);
+            }
+        }
+    }
     p.bytes = cv.off;
     return p;
 }
