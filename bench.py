@@ -21,7 +21,8 @@ Printed JSON line (one):
   merge_*      dora_merge alone (norm given): the merged inference weight,
                HBM GB/s (read W, write W').
   bwd_through_norm_us  dora_backward_through_norm (the gradient also through
-               the row norm), back-to-back launches.
+               the row norm) reusing the norm's kept W A^T, back-to-back
+               launches; *_recompute_U_us without it.
   group_norm   the factored norms of all 56 adapted projections of an 8-layer,
                8B-class decoder (hidden 4096, key/value 1024, MLP 14336,
                r 384): dora_factored_norm_grouped vs one dora_factored_norm
@@ -250,11 +251,19 @@ def main():
         # step's backward plus the norm's term in dA and dB)
         ws_t = torch.empty(D.dora_backward_through_norm_workspace(T, d_in, d_out, r, 1),
                            dtype=torch.uint8, device=dev)
+        # with the norm's U = W A^T kept by the forward (U_out), the intended
+        # pairing, and with U recomputed
+        U = torch.empty(d_out, r, dtype=torch.float32, device=dev)
+        D.dora_factored_norm(t["W"], t["A"], t["B"], s, ws=ws_n, n=n2, U_out=U)
         thru_us = timed(lambda: D.dora_backward_through_norm(
+            t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P, y, U=U, ws=ws_t,
+            out=grads))
+        thru_re_us = timed(lambda: D.dora_backward_through_norm(
             t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P, y, ws=ws_t, out=grads))
         out["bwd_through_norm_us"] = round(thru_us, 1)
-        log(f"backward through the norm {thru_us:.1f} us")
-        del ws_t
+        out["bwd_through_norm_recompute_U_us"] = round(thru_re_us, 1)
+        log(f"backward through the norm {thru_us:.1f} us (U kept), {thru_re_us:.1f} us (U recomputed)")
+        del ws_t, U
 
         # many modules: the factored norms of every adapted projection of an
         # 8-layer, 8B-class decoder (56 modules, r = 384) in grouped launches,

@@ -536,7 +536,7 @@ int run_store(bool bf16, const GPlan &p, GemmArgs a, int layout, void *out, int6
 
 int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_out, int64_t d_in,
               int64_t r, int dtype, float *n, float *base, float *cross, float *gram,
-              const NormPlan &p, char *ws, hipStream_t st)
+              const NormPlan &p, char *ws, hipStream_t st, float *U_out = nullptr)
 {
     const bool bf = dtype == DORA_BF16;
     float *gpart = reinterpret_cast<float *>(ws + p.o_gpart);
@@ -564,7 +564,24 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
         g.lde = r;
         g.rowdot = cpart;
         g.rowsq = bpart;
+        if (U_out && p.u.splits == 1) {
+            // keep U itself (fp32), written by the same product
+            g.out = U_out;
+            g.ldc = r;
+        }
         DORA_LAUNCH(run_gemm(bf, p.u, g, 0, true, st), "cross W A^T");
+        if (U_out && p.u.splits > 1) {
+            // a split product has only partial U tiles: form U once more,
+            // unsplit (no workspace), as a plain fp32 product
+            GemmArgs a = seg1(d_out, r, W, d_in, A, d_in, d_in);
+            a.mode = EPI_STORE;
+            a.out = U_out;
+            a.ldc = r;
+            a.out_f32 = 1;
+            DORA_LAUNCH(run_gemm(bf, plan_gemm(bf, nt_shape(d_out, r, d_in), kNoSplit), a, 0,
+                                 false, st),
+                        "U = W A^T");
+        }
     }
     // gram partials = rowdot(B G, B); bf16 forms B G as B G_hi + B G_lo.
     {
@@ -589,7 +606,7 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
 int forward_impl(const void *x, const void *W, const void *A, const void *B, const float *m,
                  float s, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype, void *y,
                  float *n_out, void *P_out, const float *n_in, const FwdPlan &p, char *w,
-                 hipStream_t st)
+                 hipStream_t st, float *U_out = nullptr)
 {
     const bool bf = dtype == DORA_BF16;
     // 1. the row norm (factored), unless the caller has it.
@@ -598,7 +615,7 @@ int forward_impl(const void *x, const void *W, const void *A, const void *B, con
             DORA_LAUNCH(launch_copy_f32(n_in, n_out, d_out, st), "copy n_in");
     } else {
         DORA_CHECK(norm_impl(W, A, B, s, d_out, d_in, r, dtype, n_out, nullptr, nullptr, nullptr,
-                             p.norm, w, st));
+                             p.norm, w, st, U_out));
     }
     if (T == 0)
         return DORA_OK;
@@ -1123,13 +1140,14 @@ size_t dora_backward_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r
 
 int dora_factored_norm(const void *W, const void *A, const void *B, float s, int64_t d_out,
                        int64_t d_in, int64_t r, int dtype, float *n, float *base, float *cross,
-                       float *gram, void *ws, size_t ws_bytes, void *stream)
+                       float *gram, float *U_out, void *ws, size_t ws_bytes, void *stream)
 {
     g_last_error[0] = '\0';
     DORA_CHECK(check_dtype(dtype));
     DORA_CHECK(check_dims(dtype, 0, d_in, d_out, r));
     DORA_CHECK(check_ptrs({{W, "W", true}, {A, "A", true}, {B, "B", true}, {n, "n", true},
-                           {base, "base", false}, {cross, "cross", false}, {gram, "gram", false}}));
+                           {base, "base", false}, {cross, "cross", false}, {gram, "gram", false},
+                           {U_out, "U_out", false}}));
     Carve cv;
     const NormPlan p = plan_norm(d_out, d_in, r, dtype, cv);
     DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
@@ -1138,10 +1156,11 @@ int dora_factored_norm(const void *W, const void *A, const void *B, float s, int
     const Range rws{ws, p.bytes};
     const size_t v = d_out * 4;
     DORA_CHECK(check_disjoint({{{n, v}, "n"}, {{base, v}, "base"}, {{cross, v}, "cross"},
-                               {{gram, v}, "gram"}, {rws, "workspace"}},
+                               {{gram, v}, "gram"}, {{U_out, static_cast<size_t>(d_out * r * 4)}, "U_out"},
+                               {rws, "workspace"}},
                               {{rW, "W"}, {rA, "A"}, {rB, "B"}}));
     return norm_impl(W, A, B, s, d_out, d_in, r, dtype, n, base, cross, gram, p,
-                     static_cast<char *>(ws), static_cast<hipStream_t>(stream));
+                     static_cast<char *>(ws), static_cast<hipStream_t>(stream), U_out);
 }
 
 int dora_compose(const void *base, const void *lora, const float *m, const float *n, float s,
@@ -1171,8 +1190,8 @@ int dora_compose(const void *base, const void *lora, const float *m, const float
 
 int dora_forward(const void *x, const void *W, const void *A, const void *B, const float *m,
                  float s, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtype, void *y,
-                 float *n_out, void *P_out, const float *n_in, void *ws, size_t ws_bytes,
-                 void *stream)
+                 float *n_out, void *P_out, const float *n_in, float *U_out, void *ws,
+                 size_t ws_bytes, void *stream)
 {
     g_last_error[0] = '\0';
     DORA_CHECK(check_dtype(dtype));
@@ -1180,7 +1199,10 @@ int dora_forward(const void *x, const void *W, const void *A, const void *B, con
     const bool has_t = T > 0;  // empty tensors may come with NULL data
     DORA_CHECK(check_ptrs({{x, "x", has_t}, {W, "W", true}, {A, "A", true}, {B, "B", true},
                            {m, "m", true}, {y, "y", has_t}, {n_out, "n_out", true},
-                           {P_out, "P_out", false}, {n_in, "n_in", false}}));
+                           {P_out, "P_out", false}, {n_in, "n_in", false},
+                           {U_out, "U_out", false}}));
+    if (U_out && n_in)
+        return fail(DORA_E_NULL, "U_out needs the norm computed here (n_in must be NULL)");
     const FwdPlan p = plan_forward(T, d_in, d_out, r, dtype);
     DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
     const bool bf = dtype == DORA_BF16;
@@ -1188,14 +1210,16 @@ int dora_forward(const void *x, const void *W, const void *A, const void *B, con
     const Range rx{x, T * d_in * e}, rW{W, d_out * d_in * e}, rA{A, r * d_in * e},
         rB{B, d_out * r * e}, rm{m, d_out * sizeof(float)}, rnin{n_in, d_out * sizeof(float)};
     const Range ry{y, T * d_out * e}, rn{n_out, d_out * sizeof(float)}, rP{P_out, T * r * e}, rws{ws, p.bytes};
+    const Range rU{U_out, static_cast<size_t>(d_out * r * 4)};
     if (n_in && n_in != n_out && overlap(rn, rnin))
         return fail(DORA_E_ALIAS, "n_out partially overlaps n_in");
-    DORA_CHECK(check_disjoint({{ry, "y"}, {rn, "n_out"}, {rP, "P_out"}, {rws, "workspace"}},
+    DORA_CHECK(check_disjoint({{ry, "y"}, {rn, "n_out"}, {rP, "P_out"}, {rU, "U_out"},
+                               {rws, "workspace"}},
                               {{rx, "x"}, {rW, "W"}, {rA, "A"}, {rB, "B"}, {rm, "m"}}));
     DORA_CHECK(check_disjoint({{ry, "y"}, {rP, "P_out"}, {rws, "workspace"}}, {{rnin, "n_in"}}));
 
     return forward_impl(x, W, A, B, m, s, T, d_in, d_out, r, dtype, y, n_out, P_out, n_in, p,
-                        static_cast<char *>(ws), static_cast<hipStream_t>(stream));
+                        static_cast<char *>(ws), static_cast<hipStream_t>(stream), U_out);
 }
 
 int dora_backward(const void *dy, const void *x, const void *W, const void *A, const void *B,
@@ -1261,9 +1285,10 @@ size_t dora_backward_through_norm_workspace(int64_t T, int64_t d_in, int64_t d_o
 
 int dora_backward_through_norm(const void *dy, const void *x, const void *W, const void *A,
                                const void *B, const float *m, const float *n, float s,
-                               const void *P, const void *y, int64_t T, int64_t d_in,
-                               int64_t d_out, int64_t r, int dtype, void *dx, void *dA, void *dB,
-                               float *dm, void *ws, size_t ws_bytes, void *stream)
+                               const void *P, const void *y, const float *U, int64_t T,
+                               int64_t d_in, int64_t d_out, int64_t r, int dtype, void *dx,
+                               void *dA, void *dB, float *dm, void *ws, size_t ws_bytes,
+                               void *stream)
 {
     g_last_error[0] = '\0';
     DORA_CHECK(check_dtype(dtype));
@@ -1272,7 +1297,7 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
     DORA_CHECK(check_ptrs({{dy, "dy", has_t}, {x, "x", has_t}, {W, "W", true}, {A, "A", true},
                            {B, "B", true}, {m, "m", true}, {n, "n", true}, {P, "P", has_t},
                            {y, "y", has_t}, {dx, "dx", has_t}, {dA, "dA", true}, {dB, "dB", true},
-                           {dm, "dm", true}}));
+                           {dm, "dm", true}, {U, "U", false}}));
     const ThruPlan p = plan_through_norm(T, d_in, d_out, r, dtype);
     DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
     const bool bf = dtype == DORA_BF16;
@@ -1282,7 +1307,8 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
          {{dm, d_out * sizeof(float)}, "dm"}, {{ws, p.bytes}, "workspace"}},
         {{{dy, T * d_out * e}, "dy"}, {{x, T * d_in * e}, "x"}, {{W, d_out * d_in * e}, "W"},
          {{A, r * d_in * e}, "A"}, {{B, d_out * r * e}, "B"}, {{m, d_out * sizeof(float)}, "m"},
-         {{n, d_out * sizeof(float)}, "n"}, {{P, T * r * e}, "P"}, {{y, T * d_out * e}, "y"}}));
+         {{n, d_out * sizeof(float)}, "n"}, {{P, T * r * e}, "P"}, {{y, T * d_out * e}, "y"},
+         {{U, d_out * r * sizeof(float)}, "U"}}));
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(ws);
@@ -1346,16 +1372,19 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
         DORA_CHECK(run_slots(bf, p.g, seg1(r, r, A, d_in, A, d_in, d_in), 0, gpart, 1.0f, st,
                              "dB: A A^T"));
         DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, G, st), "dB: A A^T sum");
-        DORA_CHECK(run_slots(bf, p.y1, seg1(d_out, r, W, d_in, A, d_in, d_in), 0, yslots, 1.0f,
-                             st, "dB: W A^T"));
+        // W A^T = U, the norm's own product, when the caller kept it
+        if (!U)
+            DORA_CHECK(run_slots(bf, p.y1, seg1(d_out, r, W, d_in, A, d_in, d_in), 0, yslots,
+                                 1.0f, st, "dB: W A^T"));
+        float *y2slots = U ? yslots : yslots + static_cast<size_t>(p.y1.splits) * d_out * r;
         GemmArgs g = seg1(d_out, r, B, r, G, r, r);
         if (bf) {
             g.seg[1] = GemmSeg{B, r, G + gsz, r, r};
             g.nseg = 2;
         }
-        DORA_CHECK(run_slots(bf, p.y2, g, 1, yslots + static_cast<size_t>(p.y1.splits) * d_out * r,
-                             s, st, "dB: s B G"));
-        DORA_LAUNCH(launch_combine_rows(bf, bslots, p.nb, yslots, p.ny, cs, d_out, r, dB, st),
+        DORA_CHECK(run_slots(bf, p.y2, g, 1, y2slots, s, st, "dB: s B G"));
+        DORA_LAUNCH(launch_combine_rows(bf, bslots, p.nb, yslots, U ? p.y2.splits : p.ny, cs,
+                                        d_out, r, dB, st, U),
                     "dB combine");
     }
     return DORA_OK;

@@ -25,7 +25,8 @@ struct GemmSeg {
 
 enum EpiMode : int {
     EPI_STORE = 0,   // out[m, n] = alpha * C (dtype of the kernel or fp32), split z at out + z*M*ldc
-    EPI_ROWDOT = 1,  // rowdot[(z*ntn + tn)*M + m] = sum_{n in tile} C[m, n] * E[m, n]
+    EPI_ROWDOT = 1,  // rowdot[(z*ntn + tn)*M + m] = sum_{n in tile} C[m, n] * E[m, n];
+                     // with out set, C itself as well (fp32, split z at out + z*M*ldc)
     // out[m, n] = E[m, n] + ((g_m - 1) E[m, n] + g_m alpha C[m, n]), g_m =
     // colm[m] / coln[m] (row factors here), rounded once; one split only
     EPI_MERGE = 2,
@@ -126,11 +127,12 @@ hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, i
 hipError_t launch_norm_grad_coef(int bf16, const float *m, const float *dm, const float *n, float s,
                                  const void *B, int64_t d_out, int64_t r, float *cs, void *cB,
                                  hipStream_t st);
-// out = sum_z part[z] + rowscale (.) sum_u ypart[u] ([M, N] fp32 slots; rowscale
-// nullable = 1), fixed order, rounded once to the element type.
+// out = sum_z part[z] + rowscale (.) (y0 + sum_u ypart[u]) ([M, N] fp32 slots;
+// rowscale nullable = 1, y0 nullable = 0), fixed order, rounded once to the
+// element type.
 hipError_t launch_combine_rows(int bf16, const float *part, int np, const float *ypart, int ny,
                                const float *rowscale, int64_t M, int64_t N, void *out,
-                               hipStream_t st);
+                               hipStream_t st, const float *y0 = nullptr);
 // Grouped small kernels: one launch over up to kMaxGroup modules (items
 // passed by value; blockIdx.y selects the item), the same arithmetic as the
 // single-module launchers.

@@ -345,14 +345,14 @@ __global__ void norm_grad_coef_kernel(const float *__restrict__ m, const float *
     }
 }
 
-// out[i, j] = sum_z part[z][i, j] + f_i sum_u ypart[u][i, j] (f_i = rowscale[i],
-// or 1), in this fixed order, rounded once.  VEC: 8 consecutive elements of
+// out[i, j] = sum_z part[z][i, j] + f_i (y0[i, j] + sum_u ypart[u][i, j])
+// (f_i = rowscale[i] or 1, y0 optional), in this fixed order, rounded once.  VEC: 8 consecutive elements of
 // a row per thread (N a multiple of 8).
 template <typename T, bool VEC>
 __global__ void combine_rows_kernel(const float *__restrict__ part, int np,
                                     const float *__restrict__ ypart, int ny,
                                     const float *__restrict__ rowscale, int64_t M, int64_t N,
-                                    T *__restrict__ out)
+                                    T *__restrict__ out, const float *__restrict__ y0)
 {
     const int64_t MN = M * N;
     constexpr int L = VEC ? 8 : 1;
@@ -364,6 +364,13 @@ __global__ void combine_rows_kernel(const float *__restrict__ part, int np,
 #pragma unroll
         for (int k = 0; k < L; ++k)
             a[k] = y[k] = 0.f;
+        if (y0 != nullptr) {
+            if constexpr (VEC) {
+                Vec8<float>::load(y0 + e, y);
+            } else {
+                y[0] = y0[e];
+            }
+        }
         for (int z = 0; z < np; ++z) {
             if constexpr (VEC) {
                 Vec8<float>::load(part + static_cast<int64_t>(z) * MN + e, t);
@@ -645,7 +652,7 @@ hipError_t launch_norm_grad_coef(int bf16, const float *m, const float *dm, cons
 
 hipError_t launch_combine_rows(int bf16, const float *part, int np, const float *ypart, int ny,
                                const float *rowscale, int64_t M, int64_t N, void *out,
-                               hipStream_t st)
+                               hipStream_t st, const float *y0)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
@@ -658,18 +665,18 @@ hipError_t launch_combine_rows(int bf16, const float *part, int np, const float 
         auto *o = static_cast<uint16_t *>(out);
         if (vec)
             hipLaunchKernelGGL((combine_rows_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0, st,
-                               part, np, ypart, ny, rowscale, M, N, o);
+                               part, np, ypart, ny, rowscale, M, N, o, y0);
         else
             hipLaunchKernelGGL((combine_rows_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0,
-                               st, part, np, ypart, ny, rowscale, M, N, o);
+                               st, part, np, ypart, ny, rowscale, M, N, o, y0);
     } else {
         auto *o = static_cast<float *>(out);
         if (vec)
             hipLaunchKernelGGL((combine_rows_kernel<float, true>), grid, dim3(EW_THREADS), 0, st,
-                               part, np, ypart, ny, rowscale, M, N, o);
+                               part, np, ypart, ny, rowscale, M, N, o, y0);
         else
             hipLaunchKernelGGL((combine_rows_kernel<float, false>), grid, dim3(EW_THREADS), 0, st,
-                               part, np, ypart, ny, rowscale, M, N, o);
+                               part, np, ypart, ny, rowscale, M, N, o, y0);
     }
     return hipGetLastError();
 }

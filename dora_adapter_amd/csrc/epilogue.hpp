@@ -218,6 +218,13 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
         for (int it = 0; it < ITER; ++it) {
             const int row = row0 + it * RSTEP;
             const int64_t m = mrow0 + row;
+            if (g.out != nullptr && m < M) {
+                // the product itself as well (fp32, split z at out + z M ldc)
+                float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * M * g.ldc +
+                           m * g.ldc + n;
+                for (int q = 0; q < cnt; ++q)
+                    o[q] = Cs[row * CST + c * 8 + q];
+            }
             float sum = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q)

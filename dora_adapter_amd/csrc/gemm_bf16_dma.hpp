@@ -599,6 +599,23 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) = ev[k];
         }
         __syncthreads();
+        if (g.out != nullptr) {
+            // the product itself as well (fp32, split z at out + z M ldc): per
+            // store, 32 lanes write 32 consecutive columns of one row
+            float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * g.M * g.ldc;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t row =
+                            m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                        const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
+                        if (row < g.M && col < g.N)
+                            o[row * g.ldc + col] = acc[i][j][v];
+                    }
+        }
         float *red = reinterpret_cast<float *>(smem + C::E_BYTES);  // [WN][BM]
 #pragma unroll
         for (int i = 0; i < TM; ++i) {

@@ -62,19 +62,21 @@ def lib():
         L.dora_backward_workspace.restype = sz
         L.dora_backward_workspace.argtypes = [i64, i64, i64, i64, c_int]
         L.dora_factored_norm.restype = c_int
-        L.dora_factored_norm.argtypes = [p, p, p, f, i64, i64, i64, c_int, p, p, p, p, p, sz, p]
+        L.dora_factored_norm.argtypes = [p, p, p, f, i64, i64, i64, c_int, p, p, p, p, p, p, sz,
+                                         p]
         L.dora_compose.restype = c_int
         L.dora_compose.argtypes = [p, p, p, p, f, i64, i64, c_int, p, p]
         L.dora_forward.restype = c_int
         L.dora_forward.argtypes = [p, p, p, p, p, f, i64, i64, i64, i64, c_int, p, p, p, p, p,
-                                   sz, p]
+                                   p, sz, p]
         L.dora_backward.restype = c_int
         L.dora_backward.argtypes = [p, p, p, p, p, p, p, f, p, p, i64, i64, i64, i64, c_int, p,
                                     p, p, p, p, sz, p]
         L.dora_backward_through_norm_workspace.restype = sz
         L.dora_backward_through_norm_workspace.argtypes = [i64, i64, i64, i64, c_int]
         L.dora_backward_through_norm.restype = c_int
-        L.dora_backward_through_norm.argtypes = L.dora_backward.argtypes
+        L.dora_backward_through_norm.argtypes = [p, p, p, p, p, p, p, f, p, p, p, i64, i64, i64,
+                                                 i64, c_int, p, p, p, p, p, sz, p]
         mp = ctypes.POINTER(DoraModule)
         L.dora_factored_norm_grouped_workspace.restype = sz
         L.dora_factored_norm_grouped_workspace.argtypes = [mp, c_int, c_int]
@@ -143,14 +145,15 @@ def dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype):
     return lib().dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype)
 
 
-def dora_backward_through_norm(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None):
-    """Backward with the gradient flowing through the row norm."""
-    return dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=ws, out=out, through_norm=True)
+def dora_backward_through_norm(dy, x, W, A, B, m, n, s, P, y, U=None, ws=None, out=None):
+    """Backward with the gradient flowing through the row norm (U: the
+    forward's kept W A^T, optional)."""
+    return dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=ws, out=out, through_norm=True, U=U)
 
 
-def dora_factored_norm(W, A, B, s, terms=False, ws=None, n=None):
+def dora_factored_norm(W, A, B, s, terms=False, ws=None, n=None, U_out=None):
     """Row norms of W + s*B*A (fp32 [d_out]); with terms=True also returns
-    (base, cross, gram)."""
+    (base, cross, gram).  U_out (fp32 [d_out, r]) receives W A^T."""
     dev = _dev(W)
     d_out, d_in = W.shape
     r = A.shape[0]
@@ -161,7 +164,7 @@ def dora_factored_norm(W, A, B, s, terms=False, ws=None, n=None):
     need = lib().dora_norm_workspace(d_out, d_in, r, dt)
     ws = _ws(need, dev) if ws is None else ws
     _check(lib().dora_factored_norm(_ptr(W), _ptr(A), _ptr(B), float(s), d_out, d_in, r, dt,
-                                    _ptr(n), *[_ptr(e) for e in extra], _ptr(ws),
+                                    _ptr(n), *[_ptr(e) for e in extra], _ptr(U_out), _ptr(ws),
                                     ws.numel(), _stream(dev)))
     return (n, *extra) if terms else n
 
@@ -177,8 +180,10 @@ def dora_compose(base, lora, m, n, s, y=None):
 
 
 def dora_forward(x, W, A, B, m, s, n_in=None, want_P=True, ws=None, y=None, n_out=None,
-                 P_out=None):
-    """Module forward.  Returns (y, n, P) (P is None when want_P is False)."""
+                 P_out=None, U_out=None):
+    """Module forward.  Returns (y, n, P) (P is None when want_P is False).
+    U_out (fp32 [d_out, r]) receives the norm's W A^T for the backward
+    through the norm."""
     dev = _dev(x)
     T, d_in = x.shape
     d_out = W.shape[0]
@@ -192,11 +197,11 @@ def dora_forward(x, W, A, B, m, s, n_in=None, want_P=True, ws=None, y=None, n_ou
     ws = _ws(need, dev) if ws is None else ws
     _check(lib().dora_forward(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), float(s), T, d_in,
                               d_out, r, dt, _ptr(y), _ptr(n_out), _ptr(P_out if want_P else None),
-                              _ptr(n_in), _ptr(ws), ws.numel(), _stream(dev)))
+                              _ptr(n_in), _ptr(U_out), _ptr(ws), ws.numel(), _stream(dev)))
     return y, n_out, (P_out if want_P else None)
 
 
-def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None, through_norm=False):
+def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None, through_norm=False, U=None):
     """Backward; returns dict(dx, dA, dB, dm).  The norm is detached unless
     through_norm is set (then dA and dB include the path through n)."""
     dev = _dev(W)
@@ -214,9 +219,13 @@ def dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=None, out=None, through_norm
                   if through_norm else (L.dora_backward_workspace, L.dora_backward))
     need = size(T, d_in, d_out, r, dt)
     ws = _ws(need, dev) if ws is None else ws
+    extra = (_ptr(U),) if through_norm else ()
+    if U is not None and not through_norm:
+        raise ValueError("U is used by the backward through the norm only")
     _check(call(_ptr(dy), _ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), _ptr(n), float(s),
-                _ptr(P), _ptr(y), T, d_in, d_out, r, dt, _ptr(out["dx"]), _ptr(out["dA"]),
-                _ptr(out["dB"]), _ptr(out["dm"]), _ptr(ws), ws.numel(), _stream(dev)))
+                _ptr(P), _ptr(y), *extra, T, d_in, d_out, r, dt, _ptr(out["dx"]),
+                _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dm"]), _ptr(ws), ws.numel(),
+                _stream(dev)))
     return out
 
 

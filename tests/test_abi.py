@@ -117,12 +117,12 @@ def test_compose_fp32_any_width_passes_shape_check():
 
 
 def _norm(W=FAKE, A=FAKE + (1 << 32), B=FAKE + (2 << 32), n=FAKE + (3 << 32), d_out=64,
-          d_in=128, r=8, dt=BF16, ws=FAKE + (4 << 32), ws_bytes=None, base=0):
+          d_in=128, r=8, dt=BF16, ws=FAKE + (4 << 32), ws_bytes=None, base=0, U=0):
     L = D.lib()
     if ws_bytes is None:
         ws_bytes = max(L.dora_norm_workspace(d_out, d_in, r, BF16), 1)
     return L.dora_factored_norm(_p(W), _p(A), _p(B), 1.0, d_out, d_in, r, dt, _p(n), _p(base),
-                                None, None, _p(ws), ws_bytes, None)
+                                None, None, _p(U), _p(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -131,6 +131,8 @@ def _norm(W=FAKE, A=FAKE + (1 << 32), B=FAKE + (2 << 32), n=FAKE + (3 << 32), d_
     ({"ws": 0}, E_WS), ({"ws_bytes": 16}, E_WS),
     ({"base": FAKE + (3 << 32) + 128}, E_ALIAS),       # base overlaps n
     ({"n": FAKE + 256}, E_ALIAS),                      # n inside W
+    ({"U": FAKE + (2 << 32) + 64}, E_ALIAS),           # U_out inside B
+    ({"U": FAKE + (5 << 32) + 4}, E_ALIGN),
 ])
 def test_norm_validation(kw, code):
     assert _norm(**kw) == code
@@ -138,12 +140,12 @@ def test_norm_validation(kw, code):
 
 def _fwd(x=FAKE, W=FAKE + (1 << 32), A=FAKE + (2 << 32), B=FAKE + (3 << 32),
          m=FAKE + (4 << 32), T=16, d_in=128, d_out=64, r=8, dt=BF16, y=FAKE + (5 << 32),
-         n_out=FAKE + (6 << 32), P=0, n_in=0, ws=FAKE + (7 << 32), ws_bytes=None):
+         n_out=FAKE + (6 << 32), P=0, n_in=0, ws=FAKE + (7 << 32), ws_bytes=None, U=0):
     L = D.lib()
     if ws_bytes is None:
         ws_bytes = max(L.dora_forward_workspace(T, d_in, d_out, r, BF16), 1)
     return L.dora_forward(_p(x), _p(W), _p(A), _p(B), _p(m), 1.0, T, d_in, d_out, r, dt, _p(y),
-                          _p(n_out), _p(P), _p(n_in), _p(ws), ws_bytes, None)
+                          _p(n_out), _p(P), _p(n_in), _p(U), _p(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -152,6 +154,8 @@ def _fwd(x=FAKE, W=FAKE + (1 << 32), A=FAKE + (2 << 32), B=FAKE + (3 << 32),
     ({"y": FAKE + 1024}, E_ALIAS),                     # y inside x
     ({"P": FAKE + (5 << 32) + 512}, E_ALIAS),          # P_out inside y
     ({"ws": FAKE + (2 << 32)}, E_ALIAS),               # workspace over A
+    ({"U": FAKE + (8 << 32), "n_in": FAKE + (9 << 32)}, E_NULL),  # U_out with a cached norm
+    ({"U": FAKE + (5 << 32) + 256}, E_ALIAS),          # U_out inside y
 ])
 def test_forward_validation(kw, code):
     assert _fwd(**kw) == code
@@ -170,8 +174,9 @@ def test_backward_validation(name):
                  P=base[7], y=base[8], dx=base[9], dA=base[10], dB=base[11], dm=base[12],
                  ws=base[13], ws_bytes=need, T=T)
         a.update(kw)
+        extra = (_p(a.get("U", 0)),) if name.endswith("through_norm") else ()
         return fn(_p(a["dy"]), _p(a["x"]), _p(a["W"]), _p(a["A"]), _p(a["B"]), _p(a["m"]),
-                  _p(a["n"]), 1.0, _p(a["P"]), _p(a["y"]), a["T"], d_in, d_out, r, BF16,
+                  _p(a["n"]), 1.0, _p(a["P"]), _p(a["y"]), *extra, a["T"], d_in, d_out, r, BF16,
                   _p(a["dx"]), _p(a["dA"]), _p(a["dB"]), _p(a["dm"]), _p(a["ws"]), a["ws_bytes"],
                   None)
 
@@ -183,6 +188,9 @@ def test_backward_validation(name):
     assert call(dB=base[10] + 64) == E_ALIAS            # dB inside dA
     assert call(T=-1) == E_SHAPE
     assert call(ws=base[2] + 64) == E_ALIAS             # workspace inside W
+    if name.endswith("through_norm"):
+        assert call(U=base[10] + 256) == E_ALIAS        # U inside dA
+        assert call(U=base[14] + 4) == E_ALIGN
 
 
 def test_through_norm_workspace_has_no_dense_term():

@@ -121,3 +121,41 @@ def test_through_norm_full_size_sampled():
     got_dA = np.array([float(g["dA"][k, j]) for k, j in dA_idx])
     check_close(got_dB, exp_dB, torch.bfloat16, "dB sampled")
     check_close(got_dA, exp_dA, torch.bfloat16, "dA sampled")
+
+
+@pytest.mark.parametrize("T,d_out,d_in,r,dtype,s", [
+    (300, 264, 520, 24, "bf16", 1.0),
+    (129, 512, 1024, 384, "bf16", 0.5),
+    (33, 70, 100, 5, "f32", 0.75),
+    (64, 28672, 1024, 384, "bf16", 1.0),   # W A^T unsplit: U comes from the norm's own product
+])
+def test_through_norm_with_kept_U(T, d_out, d_in, r, dtype, s):
+    """The forward keeps U = W A^T (U_out) and the backward through the norm
+    reuses it (U): U matches the plain product, the gradients match the
+    oracle, and dx, dm are those of the call that recomputes U."""
+    say("through norm with kept U", T, d_out, d_in, r, dtype)
+    mod = synth.custom(d_out, d_in, r, T, dtype, s, sigma_B=0.02, seed=T + 11, with_dy=True)
+    t = {k: gpu(mod[k]) for k in ("x", "W", "A", "B", "m", "dy")}
+    U = torch.empty(d_out, r, dtype=torch.float32, device=t["x"].device)
+    y, n, P = D.dora_forward(t["x"], t["W"], t["A"], t["B"], t["m"], s, U_out=U)
+    kept = _bwd_U(t, y, n, P, s, U)
+    fresh = _bwd(t, y, n, P, s, True)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    U_ref = np64(mod["W"]) @ np64(mod["A"]).T   # the definition of U
+    check_close(U, U_ref, torch.float32, "U", tol=2e-5)  # fp32 accumulation, not rounded
+    for k in ("dx", "dm"):
+        assert torch.equal(kept[k], fresh[k]), k
+    if d_out * d_in * T <= 2e8:
+        ref = O.backward_through_norm(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"],
+                                      mod["m"], s)
+        for k in ("dA", "dB"):
+            check_close(kept[k], ref[k], tdt, f"{k} with kept U")
+    for k in ("dA", "dB"):
+        check_close(kept[k], np64(fresh[k]), tdt, f"{k} kept U vs recomputed")
+
+
+def _bwd_U(t, y, n, P, s, U):
+    g = D.dora_backward_through_norm(t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P,
+                                     y, U=U)
+    torch.cuda.synchronize()
+    return g
