@@ -1,0 +1,48 @@
+"""GPU: the peak device memory a call adds beyond its inputs and outputs is
+its workspace, which has no d_out x d_in term.  At d_out = d_in = T = 8192,
+r = 384 (bf16) one dense [d_out, d_in] buffer would be 128 MiB; the
+factored norm's and the forward's workspaces stay far below that (the
+forward's scales with T, not with d_in), measured as the growth of torch's
+peak-allocation counter around each call with everything else allocated
+first."""
+import pytest
+import torch
+
+from dora_adapter_amd import dora as D
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+DENSE = 8192 * 8192 * 2
+
+
+def _peak_delta(fn):
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    fn()
+    torch.cuda.synchronize()
+    return torch.cuda.max_memory_allocated() - base
+
+
+@pytest.mark.parametrize("T", [8192, 2048])
+def test_transient_memory_has_no_dense_term(T):
+    say("peak memory", T)
+    d, r = 8192, 384
+    g = torch.Generator("cuda").manual_seed(3)
+    W = (torch.randn(d, d, generator=g, device="cuda") * d ** -0.5).bfloat16()
+    A = (torch.randn(r, d, generator=g, device="cuda") * d ** -0.5).bfloat16()
+    B = (torch.randn(d, r, generator=g, device="cuda") * 0.02).bfloat16()
+    m = torch.ones(d, device="cuda")
+    x = torch.randn(T, d, generator=g, device="cuda").bfloat16()
+    n = torch.empty(d, device="cuda")
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    P = torch.empty(T, r, dtype=torch.bfloat16, device="cuda")
+    norm_ws = D.dora_norm_workspace(d, d, r, 1)
+    fwd_ws = D.dora_forward_workspace(T, d, d, r, 1)
+    dn = _peak_delta(lambda: D.dora_factored_norm(W, A, B, 1.0, n=n))
+    df = _peak_delta(lambda: D.dora_forward(x, W, A, B, m, 1.0, y=y, n_out=n, P_out=P))
+    # the only allocation is the workspace (rounded up by torch's allocator)
+    assert dn <= norm_ws + (2 << 20), (dn, norm_ws)
+    assert df <= fwd_ws + (2 << 20), (df, fwd_ws)
+    assert dn < DENSE / 8 and df < DENSE / 2, (dn, df)
