@@ -7,6 +7,7 @@
 // the HIP kernels of gemm_bf16.hip, gemm_f32.hip and elementwise.hip.
 #include <stdio.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -92,6 +93,19 @@ GemmShape nt_shape(int64_t M, int64_t N, int64_t K)
     return GemmShape{M, N, {K, 0}, 1, 0, dma_operand(M, K) && dma_operand(N, K)};
 }
 
+// DORA_TILE_CFG=<index> (environment) restricts the bf16 planners to that
+// tile configuration wherever it can serve the product, so that every tile
+// shape can be run through every call; unset, the time model chooses.
+int forced_tile_cfg()
+{
+    const char *e = getenv("DORA_TILE_CFG");
+    if (e == nullptr || *e == '\0')
+        return -1;
+    char *end = nullptr;
+    const long v = strtol(e, &end, 10);
+    return (*end == '\0' && v >= 0 && v < gemm_bf16_num_cfgs()) ? static_cast<int>(v) : -1;
+}
+
 // Choose the tile configuration and the split-K count by a small time
 // model: (256-CU waves) x (one workgroup's MFMA or VALU time), plus, for a
 // split, writing and re-reading `part_per_split` fp32 values per split and
@@ -104,9 +118,15 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
     GPlan best;
     double best_cost = -1.0;
     const int ncfg = bf16 ? gemm_bf16_num_cfgs() : 1;
+    const int forced = bf16 ? forced_tile_cfg() : -1;
+    // pass 0: the forced configuration only (if any); pass 1: all of them,
+    // when pass 0 found none that serves this product
+    for (int pass = forced >= 0 ? 0 : 1; pass < 2 && best_cost < 0; ++pass)
     for (int c = 0; c < ncfg; ++c) {
         int BM, BN, bk;
         float rel;
+        if (pass == 0 && c != forced)
+            continue;
         if (bf16) {
             const TileCfg t = gemm_bf16_cfg(c);
             if ((t.dma && !sh.dma_ok) || (!t.store_ok && !sh.rowdot) || (sh.rowsq && !t.rowsq_ok))
@@ -233,7 +253,7 @@ MergePlan plan_merge(int64_t d_out, int64_t d_in, int64_t r, int dtype)
     const GemmShape sh{d_out, d_in, {r, 0}, 1, 1,
                        dma_operand(d_out, r) && dma_mn_operand(r, d_in)};
     p.g = plan_gemm(bf, sh, kNoSplit);
-    if (bf && sh.dma_ok) {
+    if (bf && sh.dma_ok && forced_tile_cfg() < 0) {
         // The product is short (K = r) and its epilogue streams W in and W'
         // out: 128 x 128 tiles keep two workgroups per CU, so one's epilogue
         // traffic overlaps the other's MFMAs (measured faster than the
@@ -699,9 +719,11 @@ GroupGemm plan_group(const std::vector<GemmShape> &sh, bool split)
     for (const GemmShape &q : sh)
         if (!q.dma_ok)
             return best;
+    const int forced = forced_tile_cfg();
+    for (int pass = forced >= 0 ? 0 : 1; pass < 2 && best_cost < 0; ++pass)
     for (int c = 0; c < gemm_bf16_num_cfgs(); ++c) {
         const TileCfg t = gemm_bf16_cfg(c);
-        if (!t.dma)
+        if (!t.dma || (pass == 0 && c != forced))
             continue;
         bool ok = true;
         int64_t zmax = split ? 32 : 1;

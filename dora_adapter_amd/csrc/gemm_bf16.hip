@@ -313,8 +313,11 @@ constexpr TileCfg kCfgs[] = {
     {256, 128, GEMM_DMA_BK, true, 0.80f, true, false},  // 4 waves (2 x 2)
     {128, 128, GEMM_DMA_BK, true, 0.80f, true, false},  // 4 waves (2 x 2), 2 per CU
     // 4 waves (1 x 4): a whole rank-384 row block per tile, so the row-dot
-    // products of the factored norm read W once; row-dot epilogue only
-    {128, 384, GEMM_DMA_BK, true, 0.95f, false, true},
+    // products of the factored norm read W once, and products with N = r
+    // (x A^T, dh B) read their long operand once
+    {128, 384, GEMM_DMA_BK, true, 0.95f, true, true},
+    // 4 waves (4 x 1): the same with M = r (Q^T x)
+    {384, 128, GEMM_DMA_BK, true, 0.95f, true, false},
 };
 
 }  // namespace
@@ -332,6 +335,7 @@ DORA_DMA_INST(256, 256, 2, 2)
 DORA_DMA_INST(256, 128, 2, 2)
 DORA_DMA_INST(128, 128, 2, 2)
 DORA_DMA_INST(128, 384, 1, 4)
+DORA_DMA_INST(384, 128, 4, 1)
 template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 1, 4, true, true, true>(GemmArgs);
 #undef DORA_DMA_INST
 #define DORA_DMA_GROUP_INST(BM, BN, WM, WN)                                                      \
@@ -343,6 +347,7 @@ DORA_DMA_GROUP_INST(256, 256, 2, 2)
 DORA_DMA_GROUP_INST(256, 128, 2, 2)
 DORA_DMA_GROUP_INST(128, 128, 2, 2)
 DORA_DMA_GROUP_INST(128, 384, 1, 4)
+DORA_DMA_GROUP_INST(384, 128, 4, 1)
 template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 1, 4, true, true, true>(
     GemmGroup);
 #undef DORA_DMA_GROUP_INST
@@ -485,6 +490,8 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
         return launch_dma_layout<128, 128, 2, 2>(a, layout, rowsq, st);
     case 7:
         return launch_dma_layout<128, 384, 1, 4>(a, layout, rowsq, st);
+    case 8:
+        return launch_dma_layout<384, 128, 4, 1>(a, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -507,6 +514,8 @@ hipError_t launch_gemm_bf16_grouped(GemmGroup &g, int layout, int cfg, bool rows
         return launch_dma_group_layout<128, 128, 2, 2>(g, layout, rowsq, st);
     case 7:
         return launch_dma_group_layout<128, 384, 1, 4>(g, layout, rowsq, st);
+    case 8:
+        return launch_dma_group_layout<384, 128, 4, 1>(g, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -41,7 +41,10 @@
 //     makes stage D + 1 visible and frees slot D (its fragments are all in
 //     registers by then), and the loads of stage D + 2 go there.  A load thus
 //     has two halves of MFMA time to land.
-//   * The epilogue is the shared LDS-staged one (epilogue.hpp).
+//   * The epilogue is the shared LDS-staged one (epilogue.hpp), a wave row
+//     (or part of one, where a whole row of 384-wide tiles would not fit)
+//     at a time; the row dots of such tiles come straight from the
+//     accumulators instead.
 #pragma once
 
 #include "dora_internal.hpp"
@@ -115,17 +118,29 @@ struct DmaCfg {
     static constexpr int B_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int OPS = 2 * STAGE_BYTES;
-    // stored epilogue: fp32 rows of the tile staged in LDS, BM / WM at a time
+    // stored epilogue: fp32 rows of the tile staged in LDS, ER at a time (a
+    // wave row's BM / WM rows, or half or a quarter of them where those do
+    // not fit), handed to epilogue_rows in column slabs of EB (its 8-column
+    // chunks must tile a wavefront: BN / 8 divides 64, else 128-wide slabs)
     static constexpr int CST = BN + 4;
-    static constexpr int EPI = (BM / WM) * CST * 4;
-    static constexpr bool STORE_OK = EPI <= 160 * 1024;
+    static constexpr int WTM_ = BM / WM;
+    static constexpr int ER = WTM_ * CST * 4 <= 160 * 1024       ? WTM_
+                              : (WTM_ / 2) * CST * 4 <= 160 * 1024 ? WTM_ / 2
+                                                                   : WTM_ / 4;
+    static_assert(ER % 32 == 0 && ER * CST * 4 <= 160 * 1024, "epilogue rows");
+    static constexpr int EPI = ER * CST * 4;
+    static constexpr int EB = 64 % (BN / 8) == 0 ? BN : 128;
+    static_assert(BN % EB == 0, "epilogue column slabs");
+    // the staged row-dot epilogue needs whole wave rows and one slab; other
+    // tiles form their row dots from the accumulators directly
+    static constexpr bool DIRECT_ROWDOT = ER != WTM_ || EB != BN;
     // row-dot epilogue: the E tile (bf16, padded rows) and one partial sum
     // per wave column and tile row
     static constexpr int EP = BN * 2 + 16;
     static constexpr int E_BYTES = BM * EP;
     static constexpr int RED_BYTES = E_BYTES + WN * BM * 4;
     static constexpr int max2(int a, int b) { return a > b ? a : b; }
-    static constexpr int SMEM = max2(max2(OPS, STORE_OK ? EPI : 0), RED_BYTES);
+    static constexpr int SMEM = max2(max2(OPS, EPI), RED_BYTES);
     static_assert(SMEM <= 160 * 1024, "LDS");
     // 1 KiB load instructions per operand tile and per wave and stage
     static constexpr int A_INST = A_BYTES / 1024, B_INST = B_BYTES / 1024;
@@ -486,7 +501,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         // the reads and loads are spread over the first SPAN MFMAs: the last
         // read then has TAIL MFMAs of time to land before the next half
         // waits for it (measured: worth it for the 1 x 4 wave layout)
-        constexpr int TAIL = WM == 1 ? 8 : 0;
+        constexpr int TAIL = (WM == 1 || WN == 1) ? 8 : 0;
         constexpr int SPAN = NMF - TAIL;
         static_assert(SPAN >= 2, "MFMA slots");
         static_for<NMF>([&](auto qc) {
@@ -573,99 +588,135 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         }
     }
 
-    if constexpr (!C::STORE_OK) {
-        // only the row-dot epilogue (the staged one does not fit in LDS)
-        // rowdot[m] = sum over this tile's columns of C[m, n] E[m, n], reduced
-        // from the accumulators: the E tile is staged in LDS, each lane forms
-        // its rows' partial sums over its columns, lanes and then wave
-        // columns are summed in a fixed order
-        constexpr int CPRow = BN / 8;
-        constexpr int NCH = BM * CPRow / NT;  // 16-byte E chunks per thread
-        static_assert((BM * CPRow) % NT == 0, "E tile chunks must split over threads");
-        const uint16_t *E = static_cast<const uint16_t *>(g.E);
-        // all loads first, so their latencies overlap
-        uint4 ev[NCH];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int idx = tid + k * NT;
-            const int64_t row = m0 + idx / CPRow, col = n0 + (idx % CPRow) * 8;
-            ev[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (row < g.M && col < g.N)
-                ev[k] = *reinterpret_cast<const uint4 *>(E + row * g.lde + col);
-        }
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int idx = tid + k * NT;
-            *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) = ev[k];
-        }
-        __syncthreads();
-        if (g.out != nullptr) {
-            // the product itself as well (fp32, split z at out + z M ldc): per
-            // store, 32 lanes write 32 consecutive columns of one row
-            float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * g.M * g.ldc;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int64_t row =
-                            m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                        const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
-                        if (row < g.M && col < g.N)
-                            o[row * g.ldc + col] = acc[i][j][v];
+    float *Cs = reinterpret_cast<float *>(smem);
+    if constexpr (C::DIRECT_ROWDOT) {
+        if (g.mode == EPI_ROWDOT) {
+            // row dots straight from the accumulators (tiles whose staged epilogue
+            // takes partial rows or column slabs)
+            // rowdot[m] = sum over this tile's columns of C[m, n] E[m, n], reduced
+            // from the accumulators: the E tile is staged in LDS, each lane forms
+            // its rows' partial sums over its columns, lanes and then wave
+            // columns are summed in a fixed order
+            constexpr int CPRow = BN / 8;
+            constexpr int NCH = BM * CPRow / NT;  // 16-byte E chunks per thread
+            static_assert((BM * CPRow) % NT == 0, "E tile chunks must split over threads");
+            const uint16_t *E = static_cast<const uint16_t *>(g.E);
+            // all loads first, so their latencies overlap
+            uint4 ev[NCH];
+    #pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const int idx = tid + k * NT;
+                const int64_t row = m0 + idx / CPRow, col = n0 + (idx % CPRow) * 8;
+                ev[k] = make_uint4(0u, 0u, 0u, 0u);
+                if (row < g.M && col < g.N)
+                    ev[k] = *reinterpret_cast<const uint4 *>(E + row * g.lde + col);
+            }
+    #pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const int idx = tid + k * NT;
+                *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) = ev[k];
+            }
+            __syncthreads();
+            if (g.out != nullptr) {
+                // the product itself as well (fp32, split z at out + z M ldc): per
+                // store, 32 lanes write 32 consecutive columns of one row
+                float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * g.M * g.ldc;
+    #pragma unroll
+                for (int i = 0; i < TM; ++i)
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j)
+    #pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int64_t row =
+                                m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                            const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
+                            if (row < g.M && col < g.N)
+                                o[row * g.ldc + col] = acc[i][j][v];
+                        }
+            }
+            float *red = reinterpret_cast<float *>(smem + C::E_BYTES);  // [WN][BM]
+    #pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                float x[16];
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rl = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                    float p = 0.f;
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int cl = wn * WTN + j * 32 + (lane & 31);
+                        const float e = bf16_to_f32(
+                            *reinterpret_cast<const uint16_t *>(smem + rl * C::EP + cl * 2));
+                        const float prod = acc[i][j][v] * e;
+                        p += n0 + cl < g.N ? prod : 0.f;
                     }
-        }
-        float *red = reinterpret_cast<float *>(smem + C::E_BYTES);  // [WN][BM]
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            float x[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rl = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                float p = 0.f;
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int cl = wn * WTN + j * 32 + (lane & 31);
-                    const float e = bf16_to_f32(
-                        *reinterpret_cast<const uint16_t *>(smem + rl * C::EP + cl * 2));
-                    const float prod = acc[i][j][v] * e;
-                    p += n0 + cl < g.N ? prod : 0.f;
+                    x[v] = p;
                 }
-                x[v] = p;
-            }
-            // Sum each of the 16 rows over the 32 lanes (columns) of a
-            // half-wave: four halving exchanges over lane bits 4..1 leave one
-            // row per lane (row index vid from those bits), summed over 16
-            // lanes; a last exchange over bit 0 completes the 32.
-#pragma unroll
-            for (int b = 4, h = 8; b >= 1; --b, h >>= 1) {
-                const bool up = (lane >> b) & 1;
-#pragma unroll
-                for (int k = 0; k < h; ++k) {
-                    const float send = up ? x[k] : x[k + h];
-                    const float keep = up ? x[k + h] : x[k];
-                    x[k] = keep + __shfl_xor(send, 1 << b);
+                // Sum each of the 16 rows over the 32 lanes (columns) of a
+                // half-wave: four halving exchanges over lane bits 4..1 leave one
+                // row per lane (row index vid from those bits), summed over 16
+                // lanes; a last exchange over bit 0 completes the 32.
+    #pragma unroll
+                for (int b = 4, h = 8; b >= 1; --b, h >>= 1) {
+                    const bool up = (lane >> b) & 1;
+    #pragma unroll
+                    for (int k = 0; k < h; ++k) {
+                        const float send = up ? x[k] : x[k + h];
+                        const float keep = up ? x[k + h] : x[k];
+                        x[k] = keep + __shfl_xor(send, 1 << b);
+                    }
                 }
+                const float tot = x[0] + __shfl_xor(x[0], 1);
+                const int vid = (((lane >> 4) & 1) << 3) | (((lane >> 3) & 1) << 2) |
+                                (((lane >> 2) & 1) << 1) | ((lane >> 1) & 1);
+                const int rl = wm * WTM + i * 32 + (vid >> 2) * 8 + (lane >> 5) * 4 + (vid & 3);
+                if ((lane & 1) == 0)
+                    red[wn * BM + rl] = tot;
             }
-            const float tot = x[0] + __shfl_xor(x[0], 1);
-            const int vid = (((lane >> 4) & 1) << 3) | (((lane >> 3) & 1) << 2) |
-                            (((lane >> 2) & 1) << 1) | ((lane >> 1) & 1);
-            const int rl = wm * WTM + i * 32 + (vid >> 2) * 8 + (lane >> 5) * 4 + (vid & 3);
-            if ((lane & 1) == 0)
-                red[wn * BM + rl] = tot;
-        }
-        __syncthreads();
-        const int ntn = static_cast<int>((g.N + BN - 1) / BN);
-        for (int r = tid; r < BM; r += NT) {
-            float sum = 0.f;
-            for (int w = 0; w < WN; ++w)
-                sum += red[w * BM + r];
-            if (m0 + r < g.M)
-                g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * g.M + m0 + r] = sum;
+            __syncthreads();
+            const int ntn = static_cast<int>((g.N + BN - 1) / BN);
+            for (int r = tid; r < BM; r += NT) {
+                float sum = 0.f;
+                for (int w = 0; w < WN; ++w)
+                    sum += red[w * BM + r];
+                if (m0 + r < g.M)
+                    g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * g.M + m0 + r] = sum;
+            }
+        } else {
+            // ER rows of a wave row at a time: that wave stages them in LDS,
+            // then every thread stores (or merges) them, EB columns per call
+            constexpr int NPASS = WTM / C::ER, TMP = C::ER / 32;
+#pragma unroll 1
+            for (int h = 0; h < WM; ++h) {
+                static_for<NPASS>([&](auto pc) __attribute__((always_inline)) {
+                    constexpr int pass = decltype(pc)::value;
+                    if (wm == h) {
+#pragma unroll
+                        for (int i = 0; i < TMP; ++i)
+#pragma unroll
+                            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) {
+                                    const int row =
+                                        i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                                    const int col = wn * WTN + j * 32 + (lane & 31);
+                                    Cs[row * C::CST + col] = acc[pass * TMP + i][j][v];
+                                }
+                    }
+                    __syncthreads();
+                    static_for<BN / C::EB>([&](auto sc) __attribute__((always_inline)) {
+                        constexpr int sl = decltype(sc)::value;
+                        epilogue_rows<C::ER, C::EB, C::CST, NT, uint16_t>(
+                            Cs + sl * C::EB, g, m0 + h * WTM + pass * C::ER, n0 + sl * C::EB, z,
+                            tn, tid);
+                    });
+                    __syncthreads();
+                });
+            }
         }
     } else {
-        float *Cs = reinterpret_cast<float *>(smem);
+        // a wave row at a time: that wave stages its rows in LDS, then every
+        // thread stores, merges or row-dots them
 #pragma unroll 1
         for (int h = 0; h < WM; ++h) {
             if (wm == h) {

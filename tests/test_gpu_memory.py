@@ -1,10 +1,10 @@
 """GPU: the peak device memory a call adds beyond its inputs and outputs is
 its workspace, which has no d_out x d_in term.  At d_out = d_in = T = 8192,
 r = 384 (bf16) one dense [d_out, d_in] buffer would be 128 MiB; the
-factored norm's and the forward's workspaces stay far below that (the
-forward's scales with T, not with d_in), measured as the growth of torch's
-peak-allocation counter around each call with everything else allocated
-first."""
+factored norm's workspace stays far below that, and the forward's, which
+scales with T, not with d_in, stays below it even at T = d_in; measured as
+the growth of torch's peak-allocation counter around each call with
+everything else allocated first."""
 import pytest
 import torch
 
@@ -45,4 +45,8 @@ def test_transient_memory_has_no_dense_term(T):
     # the only allocation is the workspace (rounded up by torch's allocator)
     assert dn <= norm_ws + (2 << 20), (dn, norm_ws)
     assert df <= fwd_ws + (2 << 20), (df, fwd_ws)
-    assert dn < DENSE / 8 and df < DENSE / 2, (dn, df)
+    # the norm's is a few MiB; the forward's is the norm's plus the fp32
+    # split-K partials of P = x A^T (a few [T, r] slices): it grows with T,
+    # and stays below one dense buffer even at T = d_in
+    assert dn < DENSE / 8 and df < DENSE, (dn, df)
+    assert df <= norm_ws + 8 * T * r * 4 + (2 << 20), (df, norm_ws)
