@@ -109,7 +109,7 @@ int forced_tile_cfg()
 // Choose the tile configuration and the split-K count by a small time
 // model: (256-CU waves) x (one workgroup's MFMA or VALU time), plus, for a
 // split, writing and re-reading `part_per_split` fp32 values per split and
-// one extra launch.  A split keeps at least 8 K steps and its partials
+// one extra launch.  A split keeps at least 512 K values and its partials
 // under 1 GiB.
 GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
 {
@@ -145,7 +145,8 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
         for (int q = 0; q < sh.nseg; ++q)
             steps += (sh.K[q] + bk - 1) / bk;
         const int64_t tiles = ((sh.M + BM - 1) / BM) * ((sh.N + BN - 1) / BN);
-        const int64_t zmax = std::min<int64_t>(32, std::max<int64_t>(steps / 8, 1));
+        // a split keeps at least 512 K values
+        const int64_t zmax = std::min<int64_t>(32, std::max<int64_t>(steps * bk / 512, 1));
         for (int64_t z = 1; z <= zmax; ++z) {
             if (z > 1 && static_cast<double>(z) * part_per_split * 4.0 > (1LL << 30))
                 break;
@@ -732,7 +733,7 @@ GroupGemm plan_group(const std::vector<GemmShape> &sh, bool split)
             int64_t steps = 0;
             for (int k = 0; k < q.nseg; ++k)
                 steps += (q.K[k] + t.bk - 1) / t.bk;
-            zmax = std::min<int64_t>(zmax, std::max<int64_t>(steps / 8, 1));
+            zmax = std::min<int64_t>(zmax, std::max<int64_t>(steps * t.bk / 512, 1));
         }
         if (!ok)
             continue;

@@ -186,31 +186,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(q, static_cast<short>(0), nrec, 0x00020000);
 }
 
-// One group of direct-to-LDS loads: instruction j moves lane l's 16 bytes at
-// rsrc + v[j] + soff + 1024 j to LDS byte lds + 1024 j + 16 l.  Issued from
-// inline asm (no register outputs; it clobbers m0 and memory) rather than
-// the builtin: the compiler treats the builtin as an LDS store and then
-// drains every such load (vmcnt(0)) before any transpose read it cannot
-// prove disjoint, which would empty the pipeline each step.  Completion is
-// covered by the kernel's explicit vmcnt waits and barriers.
-__device__ __forceinline__ void lds_dma16x4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t v0,
-                                            uint32_t v1, uint32_t v2, uint32_t v3, uint32_t soff)
+// A group of direct-to-LDS loads: set_m0 sets the group's LDS base, then
+// load J moves lane l's 16 bytes at rsrc + v + soff + 1024 J to LDS byte
+// lds + 1024 J + 16 l.  Issued from inline asm (no register outputs; memory
+// and m0 clobbered) rather than the builtin: the compiler treats the builtin
+// as an LDS store and then drains every such load (vmcnt(0)) before any
+// transpose read it cannot prove disjoint, which would empty the pipeline
+// each step.  Completion is covered by the kernel's explicit vmcnt waits and
+// barriers.  The four loads of a group go out one by one between MFMAs
+// (issued back to back they stall the wave at issue, and with it the matrix
+// core); nothing between them writes m0, which no other instruction of the
+// kernel uses.
+__device__ __forceinline__ void set_m0(uint32_t lds)
 {
-    static_assert(GROUP == 4, "one asm statement per four loads");
-    __asm__ volatile("s_mov_b32 m0, %4\n\t"
-                     "s_nop 0\n\t"
-                     "buffer_load_dwordx4 %0, %5, %6 offen lds\n\t"
-                     "buffer_load_dwordx4 %1, %5, %6 offen offset:1024 lds\n\t"
-                     "buffer_load_dwordx4 %2, %5, %6 offen offset:2048 lds\n\t"
-                     "buffer_load_dwordx4 %3, %5, %6 offen offset:3072 lds"
-                     :
-                     : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(lds), "s"(rsrc), "s"(soff)
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds) : "memory", "m0");
+}
+template <int J>
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t v, uint32_t soff)
+{
+    __asm__ volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(v), "s"(rsrc),
+                     "s"(soff), "n"(J * 1024)
                      : "memory", "m0");
 }
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // beyond every descriptor range
 
-// Load modes of a stage (see dma_group).
+// Load modes of a stage (see dma_prep).
 constexpr int LOAD_ANY = 0, LOAD_SEG0 = 1, LOAD_SEG1 = 2, LOAD_NONE = 3;
 
 // One operand's load plan: per-lane byte offsets (biased, see GROUP_BIAS)
@@ -388,11 +389,15 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     // wholly inside K of segment 0 / 1, LOAD_NONE for stages past the
     // split's end (no loads), LOAD_ANY decides per lane (a segment's tail
     // stage, whose chunks past K must load as zeros; any stage of the
-    // prologue).
-    auto dma_group = [&](int64_t sd, int d, auto mode_c) {
+    // prologue).  dma_prep sets m0 to the group's LDS base and returns its
+    // descriptor and offsets; load J of the group is then issue<J>.
+    struct Group {
+        __amdgpu_buffer_rsrc_t rs;
+        uint32_t soff;
+        uint32_t v[GROUP];
+    };
+    auto dma_prep = [&](int64_t sd, int d, auto mode_c) {
         constexpr int MODE = decltype(mode_c)::value;
-        if constexpr (MODE == LOAD_NONE)
-            return;  // a stage past this split's end: nothing reads its slot
         const bool live = MODE == LOAD_ANY ? sd < s_end : true;
         const bool sg1 = MODE == LOAD_ANY ? sd >= st1 : MODE == LOAD_SEG1;
         const int64_t kd = (sg1 ? sd - st1 : sd) * BK;
@@ -403,7 +408,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             reinterpret_cast<uintptr_t>((lds_void *)(slot(sd) + (isa ? 0 : C::A_BYTES) +
                                                      (wave * (isa ? DA::PER : DB::PER) + i0) *
                                                          1024))));
-        uint32_t v[GROUP];
+        Group grp;
+        uint32_t *v = grp.v;
         uint32_t soff;
         __amdgpu_buffer_rsrc_t rs;
         if (isa) {
@@ -435,7 +441,14 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             }
             soff = BKM ? static_cast<uint32_t>(kd * 2) : 0u;
         }
-        lds_dma16x4(rs, lds, v[0], v[1], v[2], v[3], soff);
+        grp.rs = rs;
+        grp.soff = soff;
+        set_m0(lds);
+        return grp;
+    };
+    auto issue = [&](const Group &grp, auto j_c) {
+        constexpr int J = decltype(j_c)::value;
+        lds_dma16<J>(grp.rs, grp.v[J], grp.soff);
     };
 
     f32x16_t acc[TM][TN];
@@ -483,8 +496,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     using FR = Frags<TM, TN>;
     auto half = [&](auto h_c, int64_t D, FR &cur, FR &nxt, auto mode_c) {
         constexpr int H = decltype(h_c)::value;
-        constexpr int NGH = H == 1 ? NG : 0;  // load groups in this half
-        constexpr int NOPS = NRD + NGH;
+        constexpr bool MODE_LOADS = decltype(mode_c)::value != LOAD_NONE;
+        constexpr int NLH = H == 1 && MODE_LOADS ? NG * GROUP : 0;  // loads in this half
+        constexpr int NOPS = NRD + NLH;
         // the reads of `cur` were issued during the previous half: retire
         // them here, so that no wait lands inside the interleaved sequence
         wait_lgkm0();
@@ -504,6 +518,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         constexpr int TAIL = (WM == 1 || WN == 1) ? 8 : 0;
         constexpr int SPAN = NMF - TAIL;
         static_assert(SPAN >= 2, "MFMA slots");
+        Group grp;
         static_for<NMF>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
             mfma_one<TM, TN, q>(acc, cur);
@@ -512,15 +527,19 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             constexpr int cnt = q < SPAN ? (q + 1) * NOPS / SPAN - q * NOPS / SPAN : 0;
             static_for<cnt>([&](auto oc) {
                 constexpr int o = q * NOPS / SPAN + decltype(oc)::value;
-                // load groups spread evenly, from the first slot on (they
-                // have a deadline; the reads only feed the next half)
-                constexpr int grp = (o * NGH) % NOPS < NGH ? (o * NGH) / NOPS : -1;
-                constexpr int rd = o - (o * NGH + NOPS - 1) / NOPS;
-                if constexpr (NGH > 0 && grp >= 0)
-                    dma_group(D + 2, grp, mode_c);
-                else
+                // loads spread evenly, from the first slot on (they have a
+                // deadline; the reads only feed the next half); load li is
+                // number li % GROUP of group li / GROUP
+                constexpr int li = NLH > 0 && (o * NLH) % NOPS < NLH ? (o * NLH) / NOPS : -1;
+                constexpr int rd = o - (o * NLH + NOPS - 1) / NOPS;
+                if constexpr (li >= 0) {
+                    if constexpr (li % GROUP == 0)
+                        grp = dma_prep(D + 2, li / GROUP, mode_c);
+                    issue(grp, std::integral_constant<int, li % GROUP>{});
+                } else {
                     read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, rd>(nxt, An, Bn, 1 - H, wm, wn,
                                                                     lane);
+                }
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -533,8 +552,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
-            for (int d = 0; d < NG; ++d)
-                dma_group(s_begin + p, d, std::integral_constant<int, LOAD_ANY>{});
+            for (int d = 0; d < NG; ++d) {
+                const Group grp = dma_prep(s_begin + p, d, std::integral_constant<int, LOAD_ANY>{});
+                static_for<GROUP>([&](auto jc) { issue(grp, jc); });
+            }
         wait_vmcnt<C::LPS>();  // stage s_begin has landed
         stage_barrier();
         static_for<NRD>([&](auto oc) {
