@@ -402,8 +402,12 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         const bool sg1 = MODE == LOAD_ANY ? sd >= st1 : MODE == LOAD_SEG1;
         const int64_t kd = (sg1 ? sd - st1 : sd) * BK;
         const int64_t kseg = sg1 ? g.seg[1].K : g.seg[0].K;
-        const bool isa = d < GA;
-        const int i0 = (isa ? d : d - GA) * GROUP;  // first instruction of the group
+        // groups of the operand whose loads take longer go first and get the
+        // most time to land: A (x, dh rows) for a K-major B, B (a weight
+        // read MN-major) otherwise (measured both ways on x W^T and dh W)
+        constexpr int GB = DB::PER / GROUP;
+        const bool isa = BKM ? d < GA : d >= GB;
+        const int i0 = (isa ? (BKM ? d : d - GB) : (BKM ? d - GA : d)) * GROUP;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
             reinterpret_cast<uintptr_t>((lds_void *)(slot(sd) + (isa ? 0 : C::A_BYTES) +
                                                      (wave * (isa ? DA::PER : DB::PER) + i0) *
