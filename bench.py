@@ -11,9 +11,13 @@ synthetic tensors already resident in HBM when timing starts.
 Printed JSON line (one):
   value        module forward time per step (microseconds, HIP events), the
                first quantity of the metric; ms_per_step covers forward +
-               backward, wall clock over the K timed steps.
+               backward, wall clock over the K timed steps;
+               *_min_median_max the spread over the timed steps.
+  fwd_cached_norm_us  dora_forward with the norm given (n_in), as inference
+               with frozen adapters runs it.
   compose_*    dora_compose alone, HBM GB/s with the 256 MB MALL flushed
-               before every launch (6 bytes per bf16 element).
+               before every launch (6 bytes per bf16 element);
+               compose_warm_GBps back-to-back launches without the flush.
   norm_*       dora_factored_norm alone: algorithmic flops / time against
                the 2.5 PFLOP/s dense bf16 MFMA peak.
   roofline     the dominant kernel (the base product x W^T, bf16 MFMA),
@@ -172,10 +176,17 @@ def main():
             ev[k][2].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        fwd_us = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e3
-        bwd_us = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e3
+        fwd_each = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+        bwd_each = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
+        fwd_us = sum(fwd_each) / args.steps
+        bwd_us = sum(bwd_each) / args.steps
+
+        def spread(xs):  # min, median, max over the timed steps
+            return [round(xs[0], 1), round(xs[len(xs) // 2], 1), round(xs[-1], 1)]
         out.update(value=round(fwd_us, 1), ms_per_step=round((t1 - t0) / args.steps * 1e3, 3),
                    fwd_us=round(fwd_us, 1), bwd_us=round(bwd_us, 1),
+                   fwd_us_min_median_max=spread(fwd_each),
+                   bwd_us_min_median_max=spread(bwd_each),
                    fwd_tflops=round((2 * T * d_in * d_out + 2 * T * r * (d_in + d_out)
                                      + norm_flops(d_out, d_in, r)) / fwd_us / 1e6, 1),
                    bwd_tflops=round((2 * T * d_out * d_in + 4 * T * d_out * r + 4 * T * r * d_in)
@@ -242,6 +253,13 @@ def main():
         out["norm_us"] = round(norm_us, 1)
         out["norm_mfma_util"] = round(nf / norm_us / 1e6 / PEAK_BF16_TFLOPS, 4)
         log(f"norm {norm_us:.1f} us = {nf / norm_us / 1e6:.0f} TFLOP/s")
+
+        # the forward with the norm cached (n_in: inference with frozen
+        # adapters skips the factored norm)
+        fwd_n_us = timed(lambda: D.dora_forward(t["x"], t["W"], t["A"], t["B"], t["m"], s,
+                                                n_in=n2, ws=ws_f, y=y_lin, n_out=n2, P_out=P))
+        out["fwd_cached_norm_us"] = round(fwd_n_us, 1)
+        log(f"forward with the norm cached {fwd_n_us:.1f} us")
 
         # merged weight for inference (norm given): read W, write W', 2 x 2 bytes per weight
         w_out = torch.empty_like(t["W"])
@@ -319,6 +337,9 @@ def main():
         out["compose_GBps"] = round(gbps, 1)
         out["compose_frac_hbm"] = round(gbps / PEAK_HBM_GBPS, 4)
         log(f"compose {comp_us:.1f} us = {gbps:.0f} GB/s (MALL flushed)")
+        warm_us = timed(lambda: D.dora_compose(y, lora, t["m"], n, s, y=yc))
+        out["compose_warm_GBps"] = round(6 * T * d_out / warm_us / 1e3, 1)
+        log(f"compose back to back {warm_us:.1f} us = {6 * T * d_out / warm_us / 1e3:.0f} GB/s")
         del flush, lora, yc, y_lin
 
     if args.leg == "all" and not args.no_cpu_baseline:
