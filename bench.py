@@ -88,8 +88,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the DoRA module path here has no multi-GPU mode).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the DoRA module path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
 
     import torch

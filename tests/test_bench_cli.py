@@ -1,0 +1,56 @@
+"""bench.py's host-side contract, on the CPU: more than one GPU is refused
+with a message before any device work, the peaks are the MI355X's published
+dense figures, the norm's flop count is the per-module formula written out
+term by term, and the stored counter record describes the x W^T launch it
+claims to (algorithmic bytes of that shape, write bytes = the bf16 output)."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_peaks():
+    assert bench.PEAK_BF16_TFLOPS == 2500.0
+    assert bench.PEAK_HBM_GBPS == 8000.0
+
+
+def test_norm_flops_terms():
+    d_out, d_in, r = 28672, 8192, 384
+    u = 2 * d_out * d_in * r          # U = W A^T
+    g = 2 * r * r * d_in              # G = A A^T
+    bg = 2 * (2 * d_out * r * r)      # B G_hi and B G_lo
+    base = 2 * d_out * d_in           # row sums of W^2
+    dots = 2 * (2 * d_out * r)        # cross and Gram row dots
+    assert bench.norm_flops(d_out, d_in, r) == u + g + bg + base + dots
+    # the square and MLP shapes scale the same way
+    assert bench.norm_flops(64, 128, 8) == (2 * 64 * 128 * 8 + 2 * 8 * 8 * 128 + 4 * 64 * 8 * 8
+                                            + 2 * 64 * 128 + 4 * 64 * 8)
+
+
+def test_traffic_record_describes_the_base_product():
+    with open(bench.TRAFFIC_FILE) as fh:
+        tr = json.load(fh)
+    T, d_in, d_out = 8192, 8192, 28672
+    algorithmic = 2 * (T * d_in + d_out * d_in + T * d_out)  # x, W read; y written (bf16)
+    assert tr["algorithmic_bytes_per_launch"] == algorithmic
+    cal = tr["copy_calibration"]
+    # the scaled counters reproduce the stored byte count
+    hbm = (tr["fetch_size_kib_per_launch"] * 1024 * cal["bytes"] / 1024 / cal["fetch_size_kib"]
+           + tr["write_size_kib_per_launch"] * 1024 * cal["bytes"] / 1024 / cal["write_size_kib"])
+    assert abs(hbm - tr["hbm_bytes_per_launch"]) <= 1e-6 * hbm
+    # every output byte is written once: WRITE_SIZE scaled equals the bf16 output
+    writes = tr["write_size_kib_per_launch"] * 1024 * cal["bytes"] / 1024 / cal["write_size_kib"]
+    assert abs(writes - 2 * T * d_out) <= 1e-3 * writes
+    assert len(tr["kernel_source_hash"]) == 16
