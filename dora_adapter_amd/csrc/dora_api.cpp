@@ -897,6 +897,11 @@ int norm_group_impl(const dora_module *mods, const std::vector<int> &which, int 
         memset(&fin, 0, sizeof fin);
         memset(&nf, 0, sizeof nf);
         gg.count = gu.count = gbg.count = fin.count = nf.count = cnt;
+        // the tiles of different modules share no operand rows: deal them
+        // to the XCDs in turn so each XCD gets a share of every module (in
+        // XCD runs the longest-first order gives the first XCDs all the
+        // longest products: 3.39 -> 2.88 ms on 56 decoder projections)
+        gg.spread = gu.spread = gbg.spread = 1;
         for (int k = 0; k < cnt; ++k) {
             const dora_module &md = mods[which[c.i0 + k]];
             const int64_t r = md.r, d_in = md.d_in, d_out = md.d_out;

@@ -69,6 +69,11 @@ struct GemmGroup {
     GemmArgs p[kMaxGroup];
     int tile_start[kMaxGroup + 1];
     int count;
+    // 0: each XCD takes a contiguous run of the linear workgroup ids (L2
+    // locality between neighbouring tiles); 1: ids in dispatch order, dealt
+    // to the XCDs in turn, so that every problem spreads over all of them
+    // (for problems whose tiles share no operand rows)
+    int spread;
 };
 static_assert(sizeof(GemmGroup) <= 4096, "a group must fit the kernel argument space");
 

@@ -278,7 +278,7 @@ __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN
 __device__ __forceinline__ void group_coords(const GemmGroup &grp, int BM, int BN, int &p, int &tm,
                                              int &tn, int &z)
 {
-    const int L = xcd_linear_id();
+    const int L = grp.spread ? static_cast<int>(blockIdx.x) : xcd_linear_id();
     p = 0;
     while (p + 1 < grp.count && L >= grp.tile_start[p + 1])
         ++p;
