@@ -37,7 +37,9 @@ def test_backward_full(T, d_out, d_in, r, dtype, s):
     say("backward", T, d_out, d_in, r, dtype)
     mod = synth.custom(d_out, d_in, r, T, dtype, s, sigma_B=0.02, seed=T + 1, with_dy=True)
     g, n, y, P, _ = _fwd_bwd(mod)
-    ref = O.backward_full(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], n.cpu(), s)
+    # n held constant at the oracle's own norm (the call's n is an fp32 value of it)
+    n_ref = O.norm(mod["W"], mod["A"], mod["B"], s)["n"]
+    ref = O.backward_full(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], n_ref, s)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     for k in ("dx", "dA", "dB", "dm"):
         check_close(g[k], ref[k], tdt, f"{k} {T}x{d_out}x{d_in} r{r}")
@@ -70,8 +72,9 @@ def test_training_module_full_size_sampled():
     T, d_in, d_out, r = shape.T, shape.d_in, shape.d_out, shape.r
     ix = {"dx_idx": sample_pairs(7, 30, T, d_in), "dA_idx": sample_pairs(8, 14, r, d_in),
           "dB_idx": sample_pairs(9, 30, d_out, r), "dm_idx": sample_ids(10, 14, d_out)}
+    n_ref = O.norm(mod["W"], mod["A"], mod["B"], mod["s"])["n"]  # every row: dA sums over all
     ref = O.backward_sampled(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"], mod["m"],
-                             n.cpu(), mod["s"], **ix)
+                             n_ref, mod["s"], **ix)
     got = {
         "dx": [g["dx"][t, j].item() for t, j in ix["dx_idx"]],
         "dA": [g["dA"][k, j].item() for k, j in ix["dA_idx"]],

@@ -4,11 +4,13 @@ row norm n = ||W + sBA||) vs the oracle's dense chain rule.
 Full comparisons of every gradient element at small and mid sizes (fp32 and
 bf16, widths that are not tile multiples, a rank-384 case), dx and dm equal
 bit for bit to the detached backward, determinism, the empty-token case,
+every gradient at the training module's 28672 rows (64 tokens, d_in 1024),
 and at the training module's full shape (d_in 8192 -> d_out 28672, r 384,
 8192 tokens) on sampled entries: the detached part against the oracle and
-the norm's correction against its closed form.  The oracle forms V densely
-and takes its exact row norm; the GPU call receives the factored n of its
-forward, which equals it to a few fp32 ulps."""
+the norm's correction to dB rows against its closed form from oracle
+values.  The oracle forms V densely and takes its exact row norm; the GPU
+call receives the factored n of its forward, which equals it to a few fp32
+ulps."""
 import numpy as np
 import pytest
 import torch
@@ -82,12 +84,12 @@ def test_through_norm_empty_tokens():
 def test_through_norm_full_size_sampled():
     """At the training shape the oracle cannot form every dm (that needs all
     of h = x V^T), so: dx, dm are the detached call's bits; sampled dm and
-    the detached parts of dA, dB come from the oracle; the norm's part is its
-    closed form with the coefficient cs_i = -s m_i dm_i / n_i^2, where the
-    dB rows take dm_i from the oracle and the dA columns (a sum over every
-    row) take the call's own dm:
-      dB[i,k] - dB_det[i,k] = cs_i (V_i . A_k)
-      dA[k,j] - dA_det[k,j] = sum_i cs_i B[i,k] V[i,j],  V = W + s B A."""
+    the detached parts of dA, dB come from the oracle (with its own n); the
+    norm's part of dB rows is its closed form with the coefficient
+    cs_i = -s m_i dm_i / n_i^2, dm_i and n_i from the oracle:
+      dB[i,k] - dB_det[i,k] = cs_i (V_i . A_k),  V = W + s B A.
+    The norm's part of dA sums over every row: it is checked against the
+    oracle on the training width at 64 tokens (next test)."""
     shape = synth.TRAIN_R384
     say("backward through norm full size", shape.name)
     mod = synth.make_module(shape, seed=0)
@@ -99,28 +101,34 @@ def test_through_norm_full_size_sampled():
         assert torch.equal(g[k], det[k].cpu()), k
     del t, y, P, det
     torch.cuda.empty_cache()
-    T, d_in, d_out, r = shape.T, shape.d_in, shape.d_out, shape.r
+    d_in, d_out, r = shape.d_in, shape.d_out, shape.r
+    n_ref = O.norm(mod["W"], mod["A"], mod["B"], s)["n"]
     rows = sample_ids(11, 12, d_out)
     dB_idx = [(i, k) for i in rows for k in sample_ids(12 + i, 3, r)]
     dA_idx = sample_pairs(13, 12, r, d_in)
-    n64, m64, dm_gpu = np64(n), np64(mod["m"]), np64(g["dm"])
     ref = O.backward_sampled(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"], mod["m"],
-                             n.cpu(), s, dA_idx=dA_idx, dB_idx=dB_idx, dm_idx=rows)
-    check_close(dm_gpu[rows], ref["dm"], torch.bfloat16, "dm sampled rows")
-    W64, A64, B64 = np64(mod["W"]), np64(mod["A"]), np64(mod["B"])
-    # dB rows: V_i = W_i + s B_i A, coefficient from the oracle's dm_i
-    cs_row = {i: -s * m64[i] * dmi / (n64[i] ** 2) for i, dmi in zip(rows, ref["dm"])}
+                             n_ref, s, dA_idx=dA_idx, dB_idx=dB_idx, dm_idx=rows)
+    check_close(np64(g["dm"])[rows], ref["dm"], torch.bfloat16, "dm sampled rows")
+    W64, A64, B64, m64 = np64(mod["W"]), np64(mod["A"]), np64(mod["B"]), np64(mod["m"])
+    cs_row = {i: -s * m64[i] * dmi / (n_ref[i] ** 2) for i, dmi in zip(rows, ref["dm"])}
     exp_dB = np.array([ref["dB"][q] + cs_row[i] * float((W64[i] + s * B64[i] @ A64) @ A64[k])
                        for q, (i, k) in enumerate(dB_idx)])
-    # dA columns: V[:, j] = W[:, j] + s B A[:, j], coefficient from the call's dm
-    cs_all = -s * m64 * dm_gpu / (n64 * n64)
-    exp_dA = np.array([ref["dA"][q] + float(np.dot(cs_all * B64[:, k], W64[:, j] +
-                                                     s * (B64 @ A64[:, j])))
-                       for q, (k, j) in enumerate(dA_idx)])
     got_dB = np.array([float(g["dB"][i, k]) for i, k in dB_idx])
-    got_dA = np.array([float(g["dA"][k, j]) for k, j in dA_idx])
     check_close(got_dB, exp_dB, torch.bfloat16, "dB sampled")
-    check_close(got_dA, exp_dA, torch.bfloat16, "dA sampled")
+
+
+def test_through_norm_training_width_64_tokens():
+    """Every gradient against the oracle at the training module's d_out
+    (28672 rows, r 384) on 64 tokens and d_in 1024: the norm's part of dA is
+    a sum over all 28672 rows (cs B)^T V."""
+    say("backward through norm, 28672 rows, 64 tokens")
+    mod = synth.custom(28672, 1024, 384, 64, "bf16", 1.0, sigma_B=0.02, seed=65, with_dy=True)
+    t, y, n, P = _fwd(mod)
+    g = _bwd(t, y, n, P, 1.0, True)
+    ref = O.backward_through_norm(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"], mod["m"],
+                                  1.0)
+    for k in ("dx", "dA", "dB", "dm"):
+        check_close(g[k], ref[k], torch.bfloat16, f"{k} 64x28672x1024 r384")
 
 
 @pytest.mark.parametrize("T,d_out,d_in,r,dtype,s", [

@@ -84,6 +84,6 @@ def test_negative_scale_and_magnitudes_of_both_signs():
 def test_large_scale():
     say("large s")
     mod = synth.custom(520, 1032, 40, 130, "bf16", 16.0, sigma_B=0.02, seed=35, with_dy=True)
-    _, n, _, _ = _check_all(mod, 16.0, "s=16")
-    g = np64(mod["m"]) / np64(n)
+    _check_all(mod, 16.0, "s=16")
+    g = np64(mod["m"]) / O.norm(mod["W"], mod["A"], mod["B"], 16.0)["n"]
     assert g.max() < 0.9, "the case is meant to leave the near-unity regime"
