@@ -605,17 +605,39 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
         }
     }
     // gram partials = rowdot(B G, B); bf16 forms B G as B G_hi + B G_lo.
+    // With U_out, the same product adds s B G to the kept U: U_out then holds
+    // V A^T = (W + s B A) A^T = U + s B G (an unsplit product: one writer per
+    // element; a split one leaves it to an unsplit fp32 product).
     {
         GemmArgs g = seg1(d_out, r, B, r, gfin, r, r);
         if (bf) {
             g.seg[1] = GemmSeg{B, r, static_cast<const uint16_t *>(gfin) + r * r, r, r};
             g.nseg = 2;
         }
+        GemmArgs a = g;
         g.mode = EPI_ROWDOT;
         g.E = B;
         g.lde = r;
         g.rowdot = gmpart;
+        if (U_out && p.bg.splits == 1) {
+            g.out = U_out;
+            g.ldc = r;
+            g.out_accum = 1;
+            g.alpha = s;
+        }
         DORA_LAUNCH(run_gemm(bf, p.bg, g, 1, false, st), "gram B G");
+        if (U_out && p.bg.splits > 1) {
+            a.mode = EPI_STORE;
+            a.out = U_out;
+            a.ldc = r;
+            a.out_f32 = 1;
+            a.out_accum = 1;
+            a.alpha = s;
+            const GemmShape bgs{d_out, r, {r, r}, bf ? 2 : 1, 1,
+                                dma_operand(d_out, r) && dma_mn_operand(r, r)};
+            DORA_LAUNCH(run_gemm(bf, plan_gemm(bf, bgs, kNoSplit), a, 1, false, st),
+                        "V A^T += s B G");
+        }
     }
     DORA_LAUNCH(launch_norm_finish(bpart, p.u.splits, cpart, p.u.splits * p.u.ntn, gmpart,
                                    p.bg.splits * p.bg.ntn, d_out, s, n, base, cross, gram, st),
@@ -1391,28 +1413,31 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
                                         p.z.splits, nullptr, r, d_in, dA, st),
                     "dA combine");
     }
-    // 6. dB = s dh^T P + cs (.) (W A^T + s B G),  G = A A^T.
+    // 6. dB = s dh^T P + cs (.) V A^T,  V A^T = W A^T + s B G,  G = A A^T.
     {
         DORA_CHECK(run_slots(bf, b.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, bslots, s, st,
                              "dB: s dh^T P"));
-        float *gpart = reinterpret_cast<float *>(w + p.o_gpart);
-        char *G = w + p.o_gfin;
-        DORA_CHECK(run_slots(bf, p.g, seg1(r, r, A, d_in, A, d_in, d_in), 0, gpart, 1.0f, st,
-                             "dB: A A^T"));
-        DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, G, st), "dB: A A^T sum");
-        // W A^T = U, the norm's own product, when the caller kept it
-        if (!U)
+        // V A^T = W A^T + s B G: the norm's own product when the caller kept it
+        // (U), else formed here
+        if (!U) {
+            float *gpart = reinterpret_cast<float *>(w + p.o_gpart);
+            char *G = w + p.o_gfin;
+            DORA_CHECK(run_slots(bf, p.g, seg1(r, r, A, d_in, A, d_in, d_in), 0, gpart, 1.0f,
+                                 st, "dB: A A^T"));
+            DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, G, st), "dB: A A^T sum");
             DORA_CHECK(run_slots(bf, p.y1, seg1(d_out, r, W, d_in, A, d_in, d_in), 0, yslots,
                                  1.0f, st, "dB: W A^T"));
-        float *y2slots = U ? yslots : yslots + static_cast<size_t>(p.y1.splits) * d_out * r;
-        GemmArgs g = seg1(d_out, r, B, r, G, r, r);
-        if (bf) {
-            g.seg[1] = GemmSeg{B, r, G + gsz, r, r};
-            g.nseg = 2;
+            GemmArgs g = seg1(d_out, r, B, r, G, r, r);
+            if (bf) {
+                g.seg[1] = GemmSeg{B, r, G + gsz, r, r};
+                g.nseg = 2;
+            }
+            DORA_CHECK(run_slots(bf, p.y2, g, 1,
+                                 yslots + static_cast<size_t>(p.y1.splits) * d_out * r, s, st,
+                                 "dB: s B G"));
         }
-        DORA_CHECK(run_slots(bf, p.y2, g, 1, y2slots, s, st, "dB: s B G"));
-        DORA_LAUNCH(launch_combine_rows(bf, bslots, p.nb, yslots, U ? p.y2.splits : p.ny, cs,
-                                        d_out, r, dB, st, U),
+        DORA_LAUNCH(launch_combine_rows(bf, bslots, p.nb, yslots, U ? 0 : p.ny, cs, d_out, r, dB,
+                                        st, U),
                     "dB combine");
     }
     return DORA_OK;

@@ -43,6 +43,9 @@ struct GemmArgs {
     void *out;
     int64_t ldc;
     int out_f32;             // 1: fp32 output (split-K partials); 0: kernel dtype
+    // fp32 output only: 1 adds to what `out` holds instead of overwriting
+    // it (one writer per element: unsplit products only)
+    int out_accum;
     float alpha;
     // optional per-column magnitude scale of the store: with colm and coln
     // set, column n of alpha * C is stored as h + ((colm[n] - coln[n]) /

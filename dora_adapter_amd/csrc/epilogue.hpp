@@ -130,7 +130,10 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
             if (g.out_f32) {
                 float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * M * g.ldc +
                            m * g.ldc + n;
-                if (cnt == 8 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
+                if (g.out_accum) {
+                    for (int q = 0; q < cnt; ++q)
+                        o[q] += v[q];
+                } else if (cnt == 8 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
                     reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
                     reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
                 } else {
@@ -219,11 +222,13 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
             const int row = row0 + it * RSTEP;
             const int64_t m = mrow0 + row;
             if (g.out != nullptr && m < M) {
-                // the product itself as well (fp32, split z at out + z M ldc)
+                // the product itself as well (fp32, split z at out + z M ldc;
+                // with out_accum, alpha times it added to what out holds)
                 float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * M * g.ldc +
                            m * g.ldc + n;
                 for (int q = 0; q < cnt; ++q)
-                    o[q] = Cs[row * CST + c * 8 + q];
+                    o[q] = g.out_accum ? o[q] + g.alpha * Cs[row * CST + c * 8 + q]
+                                       : Cs[row * CST + c * 8 + q];
             }
             float sum = 0.f;
 #pragma unroll

@@ -628,7 +628,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             const uint16_t *E = static_cast<const uint16_t *>(g.E);
             // all loads first, so their latencies overlap
             uint4 ev[NCH];
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < NCH; ++k) {
                 const int idx = tid + k * NT;
                 const int64_t row = m0 + idx / CPRow, col = n0 + (idx % CPRow) * 8;
@@ -636,38 +636,42 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 if (row < g.M && col < g.N)
                     ev[k] = *reinterpret_cast<const uint4 *>(E + row * g.lde + col);
             }
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < NCH; ++k) {
                 const int idx = tid + k * NT;
                 *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) = ev[k];
             }
             __syncthreads();
             if (g.out != nullptr) {
-                // the product itself as well (fp32, split z at out + z M ldc): per
+                // the product itself as well (fp32, split z at out + z M ldc;
+                // with out_accum, alpha times it added to what out holds): per
                 // store, 32 lanes write 32 consecutive columns of one row
                 float *o = static_cast<float *>(g.out) + static_cast<int64_t>(z) * g.M * g.ldc;
-    #pragma unroll
+                const bool accum = g.out_accum != 0;
+#pragma unroll
                 for (int i = 0; i < TM; ++i)
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < TN; ++j)
-    #pragma unroll
+#pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int64_t row =
                                 m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
                             const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
                             if (row < g.M && col < g.N)
-                                o[row * g.ldc + col] = acc[i][j][v];
+                                o[row * g.ldc + col] =
+                                    accum ? o[row * g.ldc + col] + g.alpha * acc[i][j][v]
+                                          : acc[i][j][v];
                         }
             }
             float *red = reinterpret_cast<float *>(smem + C::E_BYTES);  // [WN][BM]
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < TM; ++i) {
                 float x[16];
-    #pragma unroll
+#pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int rl = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
                     float p = 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < TN; ++j) {
                         const int cl = wn * WTN + j * 32 + (lane & 31);
                         const float e = bf16_to_f32(
@@ -681,10 +685,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 // half-wave: four halving exchanges over lane bits 4..1 leave one
                 // row per lane (row index vid from those bits), summed over 16
                 // lanes; a last exchange over bit 0 completes the 32.
-    #pragma unroll
+#pragma unroll
                 for (int b = 4, h = 8; b >= 1; --b, h >>= 1) {
                     const bool up = (lane >> b) & 1;
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < h; ++k) {
                         const float send = up ? x[k] : x[k + h];
                         const float keep = up ? x[k + h] : x[k];

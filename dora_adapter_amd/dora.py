@@ -147,13 +147,14 @@ def dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype):
 
 def dora_backward_through_norm(dy, x, W, A, B, m, n, s, P, y, U=None, ws=None, out=None):
     """Backward with the gradient flowing through the row norm (U: the
-    forward's kept W A^T, optional)."""
+    forward's kept V A^T = W A^T + s B A A^T, optional)."""
     return dora_backward(dy, x, W, A, B, m, n, s, P, y, ws=ws, out=out, through_norm=True, U=U)
 
 
 def dora_factored_norm(W, A, B, s, terms=False, ws=None, n=None, U_out=None):
     """Row norms of W + s*B*A (fp32 [d_out]); with terms=True also returns
-    (base, cross, gram).  U_out (fp32 [d_out, r]) receives W A^T."""
+    (base, cross, gram).  U_out (fp32 [d_out, r]) receives
+    V A^T = W A^T + s B A A^T."""
     dev = _dev(W)
     d_out, d_in = W.shape
     r = A.shape[0]
@@ -182,8 +183,8 @@ def dora_compose(base, lora, m, n, s, y=None):
 def dora_forward(x, W, A, B, m, s, n_in=None, want_P=True, ws=None, y=None, n_out=None,
                  P_out=None, U_out=None):
     """Module forward.  Returns (y, n, P) (P is None when want_P is False).
-    U_out (fp32 [d_out, r]) receives the norm's W A^T for the backward
-    through the norm."""
+    U_out (fp32 [d_out, r]) receives the norm's V A^T = W A^T + s B A A^T for
+    the backward through the norm."""
     dev = _dev(x)
     T, d_in = x.shape
     d_out = W.shape[0]

@@ -102,9 +102,11 @@ size_t dora_backward_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r
  * zero only when ||W_i + s B_i A|| << ||W_i||).
  *   W [d_out, d_in], A [r, d_in], B [d_out, r] in `dtype`.
  *   n [d_out] fp32 (required).  base, cross, gram [d_out] fp32, each
- *   optional (NULL to skip).  U_out [d_out, r] fp32, optional: receives U
- *   itself (the intermediate is formed anyway; keeping it lets the backward
- *   through the norm skip its own W A^T product).
+ *   optional (NULL to skip).  U_out [d_out, r] fp32, optional: receives
+ *   V A^T = (W + s B A) A^T = U + s B G, the two products the norm forms
+ *   anyway (U by the cross term's product, s B G added by the Gram term's);
+ *   keeping it lets the backward through the norm skip W A^T, A A^T and
+ *   B G (its dB term is a row scale of exactly this matrix).
  *   ws: device scratch of dora_norm_workspace(d_out, d_in, r, dtype) bytes.
  */
 int dora_factored_norm(const void *W, const void *A, const void *B, float s,
@@ -146,8 +148,9 @@ int dora_compose(const void *base, const void *lora, const float *m, const float
  *   the workspace only).
  *   n_in [d_out] fp32 or NULL: a norm computed earlier (cached inference);
  *   when given, the norm is not recomputed.
- *   U_out [d_out, r] fp32 or NULL: receives the norm's U = W A^T (as in
- *   dora_factored_norm) for dora_backward_through_norm; needs n_in NULL.
+ *   U_out [d_out, r] fp32 or NULL: receives the norm's V A^T = U + s B G
+ *   (as in dora_factored_norm) for dora_backward_through_norm; needs n_in
+ *   NULL.
  *   y must not overlap any input, n_out, P_out or U_out.
  */
 int dora_forward(const void *x, const void *W, const void *A, const void *B, const float *m,
@@ -194,9 +197,11 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
  * dora_backward, bit for bit.  Arguments, layouts, aliasing rules and the
  * T = 0 case (dm zero, dA and dB then zero as well) are those of
  * dora_backward; n is the norm dora_forward returned and is taken as the
- * exact norm of W + s B A.  U [d_out, r] fp32 or NULL: the norm's W A^T as
- * dora_forward's U_out kept it (the factored norm reuses it, so the W A^T
- * product is not formed again); NULL recomputes it.
+ * exact norm of W + s B A.  U [d_out, r] fp32 or NULL: the norm's
+ * V A^T = W A^T + s B (A A^T) as dora_forward's (or dora_factored_norm's)
+ * U_out kept it, for the same W, A, B and s (the factored norm's products
+ * are reused, so W A^T, A A^T and B G are not formed again); NULL forms
+ * them here.
  *   ws: dora_backward_through_norm_workspace(T, d_in, d_out, r, dtype) bytes.
  */
 size_t dora_backward_through_norm_workspace(int64_t T, int64_t d_in, int64_t d_out, int64_t r,

@@ -135,12 +135,12 @@ def test_through_norm_training_width_64_tokens():
     (300, 264, 520, 24, "bf16", 1.0),
     (129, 512, 1024, 384, "bf16", 0.5),
     (33, 70, 100, 5, "f32", 0.75),
-    (64, 28672, 1024, 384, "bf16", 1.0),   # W A^T unsplit: U comes from the norm's own product
+    (64, 28672, 1024, 384, "bf16", 1.0),   # unsplit: V A^T written by the norm's own products
 ])
 def test_through_norm_with_kept_U(T, d_out, d_in, r, dtype, s):
-    """The forward keeps U = W A^T (U_out) and the backward through the norm
-    reuses it (U): U matches the plain product, the gradients match the
-    oracle, and dx, dm are those of the call that recomputes U."""
+    """The forward keeps V A^T = W A^T + s B A A^T (U_out) and the backward
+    through the norm reuses it (U): it matches its definition, the gradients
+    match the oracle, and dx, dm are those of the call that forms it anew."""
     say("through norm with kept U", T, d_out, d_in, r, dtype)
     mod = synth.custom(d_out, d_in, r, T, dtype, s, sigma_B=0.02, seed=T + 11, with_dy=True)
     t = {k: gpu(mod[k]) for k in ("x", "W", "A", "B", "m", "dy")}
@@ -149,8 +149,11 @@ def test_through_norm_with_kept_U(T, d_out, d_in, r, dtype, s):
     kept = _bwd_U(t, y, n, P, s, U)
     fresh = _bwd(t, y, n, P, s, True)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
-    U_ref = np64(mod["W"]) @ np64(mod["A"]).T   # the definition of U
-    check_close(U, U_ref, torch.float32, "U", tol=2e-5)  # fp32 accumulation, not rounded
+    W64, A64, B64 = np64(mod["W"]), np64(mod["A"]), np64(mod["B"])
+    U_ref = (W64 + s * B64 @ A64) @ A64.T   # the definition: V A^T
+    # fp32 accumulation, not rounded; the s B G part carries G as a bf16
+    # hi / lo pair (about 16 significant bits)
+    check_close(U, U_ref, torch.float32, "V A^T", tol=1e-4)
     for k in ("dx", "dm"):
         assert torch.equal(kept[k], fresh[k]), k
     if d_out * d_in * T <= 2e8:

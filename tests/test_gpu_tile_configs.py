@@ -46,7 +46,8 @@ def _reference(shape):
                "det": O.backward_full(mod["dy"], *args, n, s),
                "thru": O.backward_through_norm(mod["dy"], *args, s),
                "merge": O.merge(mod["W"], mod["A"], mod["B"], mod["m"], s),
-               "U": np64(mod["W"]) @ np64(mod["A"]).T,   # the definitions of U and P
+               # the definitions of the kept V A^T and of P
+               "U": (np64(mod["W"]) + s * np64(mod["B"]) @ np64(mod["A"])) @ np64(mod["A"]).T,
                "P": np64(mod["x"]) @ np64(mod["A"]).T}
         # a sibling module: B halved (exact in bf16)
         ref["B2"] = (mod["B"].float() * 0.5).to(torch.bfloat16)
@@ -82,7 +83,7 @@ def test_every_call_on_tile_config(tile_cfg, shape):
     torch.cuda.synchronize()
     check_norm(n, ref["n"], bf, f"n {tag}")
     check_close(y, ref["y"], bf, f"y {tag}")
-    check_close(U, ref["U"], torch.float32, f"U {tag}", tol=2e-5)
+    check_close(U, ref["U"], torch.float32, f"V A^T {tag}", tol=1e-4)
 
     det = D.dora_backward(t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P, y)
     thru = D.dora_backward(t["dy"], t["x"], t["W"], t["A"], t["B"], t["m"], n, s, P, y,
