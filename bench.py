@@ -81,9 +81,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--leg", choices=["all", "step", "kernels", "base", "copy"], default="all",
-                    help="'base' launches only the dominant kernel (for counter runs); "
-                         "'copy' a plain device copy of known size (counter calibration)")
+    ap.add_argument("--leg", choices=["all", "step", "kernels", "base", "compose", "copy"],
+                    default="all",
+                    help="'base' launches only the dominant kernel, 'compose' only dora_compose "
+                         "(for counter runs); 'copy' a plain device copy of known size "
+                         "(counter calibration)")
     ap.add_argument("--iters", type=int, default=10, help="launches per kernel-leg timing")
     args = ap.parse_args()
 
@@ -126,6 +128,20 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"leg": "base", "launches": KERNEL_WARMUP + args.iters,
                           "flops_per_launch": 2 * T * d_in * d_out}))
+        return
+
+    if args.leg == "compose":
+        # dora_compose alone on the training module's [T, d_out] (6 bytes per
+        # bf16 element: read base and lora, write y)
+        base = torch.randn(T, d_out, device=dev).bfloat16()
+        lora = torch.randn(T, d_out, device=dev).bfloat16()
+        n = torch.rand(d_out, device=dev) + 0.5
+        yc = torch.empty_like(base)
+        for _ in range(KERNEL_WARMUP + args.iters):
+            D.dora_compose(base, lora, t["m"], n, s, y=yc)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "compose", "launches": KERNEL_WARMUP + args.iters,
+                          "bytes_per_launch": 6 * T * d_out + 8 * d_out}))
         return
 
     # Preallocated outputs and workspaces: nothing is allocated inside the step.
