@@ -81,11 +81,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--leg", choices=["all", "step", "kernels", "base", "compose", "copy"],
+    ap.add_argument("--leg", choices=["all", "step", "kernels", "base", "norm", "compose",
+                                      "copy"],
                     default="all",
-                    help="'base' launches only the dominant kernel, 'compose' only dora_compose "
-                         "(for counter runs); 'copy' a plain device copy of known size "
-                         "(counter calibration)")
+                    help="'base' launches only the dominant kernel, 'norm' only "
+                         "dora_factored_norm, 'compose' only dora_compose (for counter runs); "
+                         "'copy' a plain device copy of known size (counter calibration)")
     ap.add_argument("--iters", type=int, default=10, help="launches per kernel-leg timing")
     args = ap.parse_args()
 
@@ -128,6 +129,19 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"leg": "base", "launches": KERNEL_WARMUP + args.iters,
                           "flops_per_launch": 2 * T * d_in * d_out}))
+        return
+
+    if args.leg == "norm":
+        # dora_factored_norm alone on the training module (W A^T with the row
+        # sums of squares and row dots, A A^T, B G, the finish)
+        n = torch.empty(d_out, dtype=torch.float32, device=dev)
+        ws_n = torch.empty(D.dora_norm_workspace(d_out, d_in, r, 1), dtype=torch.uint8,
+                           device=dev)
+        for _ in range(KERNEL_WARMUP + args.iters):
+            D.dora_factored_norm(t["W"], t["A"], t["B"], s, ws=ws_n, n=n)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "norm", "launches": KERNEL_WARMUP + args.iters,
+                          "flops_per_launch": norm_flops(d_out, d_in, r)}))
         return
 
     if args.leg == "compose":
