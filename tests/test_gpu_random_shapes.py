@@ -2,15 +2,23 @@
 against the oracle, on widths that land anywhere relative to the tile and
 K-stage sizes (tails in either K segment, single partial tiles, split-K
 chosen or not by the planner).  Every case is a full comparison of every
-output element."""
+output element.
+
+With a bf16 module and only a few tokens (T <= 8), dA and dB are sums of a
+handful of products of bf16-stored operands (dh, P, Q, c B); when those few
+terms cancel, their rounding alone can exceed 2e-2 rms(ref), so there an
+element may instead lie within the a-priori rounding bound of those operands
+(gpu_util.reduction_bound_bf16, pinned on the CPU in test_rounding_bound.py).
+Seeds 134, 149, 160 and 190 are such cases."""
 import random
 
+import numpy as np
 import pytest
 import torch
 
 from dora_adapter_amd import dora as D
 from dora_adapter_amd import synth
-from gpu_util import check_close, check_norm, gpu, say
+from gpu_util import U_BF16, check_close, check_norm, gpu, reduction_bound_bf16, say
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +36,10 @@ def _shape(seed):
     return T, d_out, d_in, r, dtype, s
 
 
-@pytest.mark.parametrize("seed", range(12))
+FEW_TOKENS = 8
+
+
+@pytest.mark.parametrize("seed", list(range(12)) + [134, 149, 160, 190])
 def test_random_shape(seed):
     T, d_out, d_in, r, dtype, s = _shape(seed)
     say("random shape", seed, T, d_out, d_in, r, dtype, s)
@@ -48,7 +59,17 @@ def test_random_shape(seed):
                               ref_n, s)
     ref_thru = O.backward_through_norm(mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"],
                                        mod["m"], s)
+    bounds = {}
+    if dtype == "bf16" and T <= FEW_TOKENS:
+        args = (mod["dy"], mod["x"], mod["W"], mod["A"], mod["B"], mod["m"], ref_n,
+                ref_det["dm"], s)
+        for path, ref in (("det", ref_det), ("thru", ref_thru)):
+            bA, bB = reduction_bound_bf16(*args, path == "thru")
+            bounds[path] = {"dA": bA + U_BF16 * np.abs(ref["dA"]),
+                            "dB": bB + U_BF16 * np.abs(ref["dB"])}
     for k in ("dx", "dA", "dB", "dm"):
-        check_close(det[k], ref_det[k], tdt, f"detached {k}")
-        check_close(thru[k], ref_thru[k], tdt, f"through-norm {k}")
+        check_close(det[k], ref_det[k], tdt, f"detached {k}",
+                    bound=bounds.get("det", {}).get(k))
+        check_close(thru[k], ref_thru[k], tdt, f"through-norm {k}",
+                    bound=bounds.get("thru", {}).get(k))
     check_close(merged, O.merge(mod["W"], mod["A"], mod["B"], mod["m"], s), tdt, "merge")
