@@ -74,6 +74,11 @@ struct GemmShape {
 // up to 3 KiB (grouped loads); keep every operand's range below 2 GiB - 4 KiB.
 constexpr int64_t kDmaBytes = (1LL << 31) - 4096;
 constexpr double kWaveOverhead = 8e-6;  // seconds per wave of workgroups
+// Extra seconds per wave when a row-dot epilogue stages the tile through LDS
+// instead of dotting the accumulators directly (measured on the r-wide B G
+// product of the norm at d_out 28672, r 384: 58.8 us on 256 x 256 tiles
+// against 39.3 us on 128 x 384 ones, at equal tile counts and K steps).
+constexpr double kStagedRowdotOverhead = 20e-6;
 
 // Operands the direct-to-LDS kernel can take (bf16, byte offsets < 2 GiB):
 // a K-major one of `rows` x `K` loads whole 16-byte chunks (K % 8) and zeros
@@ -154,10 +159,11 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
             const int64_t waves = std::max<int64_t>((tiles * z + kCUs - 1) / kCUs, 1);
             // a wave of workgroups also pays its pipeline fill and epilogue
             // (measured: about 8 us on the row-dot products of the norm)
+            const bool staged_rowdot = sh.rowdot && !(bf16 && gemm_bf16_cfg(c).direct_rowdot);
             double cost = static_cast<double>(waves) *
                           (2.0 * BM * BN * bk * static_cast<double>(std::max<int64_t>(sps, 1)) /
                                (cu_flops * rel) +
-                           kWaveOverhead);
+                           kWaveOverhead + (staged_rowdot ? kStagedRowdotOverhead : 0.0));
             if (z > 1)
                 cost += 2.0 * z * part_per_split * 4.0 / hbm + 3e-6;
             if (best_cost < 0 || cost < best_cost * 0.97) {
@@ -748,10 +754,11 @@ GroupGemm plan_group(const std::vector<GemmShape> &sh, bool split)
         const TileCfg t = gemm_bf16_cfg(c);
         if (!t.dma || (pass == 0 && c != forced))
             continue;
-        bool ok = true;
+        bool ok = true, rowdot = false;
         int64_t zmax = split ? 32 : 1;
         for (const GemmShape &q : sh) {
             ok = ok && (t.store_ok || q.rowdot) && (!q.rowsq || t.rowsq_ok);
+            rowdot = rowdot || q.rowdot;
             int64_t steps = 0;
             for (int k = 0; k < q.nseg; ++k)
                 steps += (q.K[k] + t.bk - 1) / t.bk;
@@ -774,7 +781,10 @@ GroupGemm plan_group(const std::vector<GemmShape> &sh, bool split)
                 longest = std::max(longest, tile_time);
             }
             const int64_t waves = std::max<int64_t>((tiles + kCUs - 1) / kCUs, 1);
-            const double cost = std::max(work / kCUs, longest) + waves * kWaveOverhead;
+            const double cost =
+                std::max(work / kCUs, longest) +
+                waves * (kWaveOverhead +
+                         (rowdot && !t.direct_rowdot ? kStagedRowdotOverhead : 0.0));
             if (best_cost < 0 || cost < best_cost * 0.97) {
                 best_cost = cost;
                 best.cfg = c;

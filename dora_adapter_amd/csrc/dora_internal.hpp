@@ -102,6 +102,7 @@ struct TileCfg {
     float rel_speed;  // relative throughput of a full tile, for planning
     bool store_ok;    // EPI_STORE supported (else EPI_ROWDOT only)
     bool rowsq_ok;    // row sums of squares of A supported
+    bool direct_rowdot;  // EPI_ROWDOT formed from the accumulators (no LDS staging)
 };
 int gemm_bf16_num_cfgs();
 TileCfg gemm_bf16_cfg(int cfg);

@@ -308,19 +308,19 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
 // rate they reach as one wave of tiles on the rank-r products (x A^T,
 // dh^T P, Q^T x at the training shape).
 constexpr TileCfg kCfgs[] = {
-    {256, 256, GEMM_BK, false, 0.76f, true, true},
-    {256, 128, GEMM_BK, false, 0.68f, true, true},
-    {128, 128, GEMM_BK, false, 0.56f, true, true},
-    {128, 64, GEMM_BK, false, 0.40f, true, true},
-    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false},  // 4 waves (2 x 2), 128 x 128 per wave
-    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false},  // 4 waves (2 x 2)
-    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false},  // 4 waves (2 x 2), 2 per CU
+    {256, 256, GEMM_BK, false, 0.76f, true, true, false},
+    {256, 128, GEMM_BK, false, 0.68f, true, true, false},
+    {128, 128, GEMM_BK, false, 0.56f, true, true, false},
+    {128, 64, GEMM_BK, false, 0.40f, true, true, false},
+    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false, false},  // 4 waves (2 x 2), 128 x 128 per wave
+    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false, false},  // 4 waves (2 x 2)
+    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false, false},  // 4 waves (2 x 2), 2 per CU
     // 4 waves (1 x 4): a whole rank-384 row block per tile, so the row-dot
     // products of the factored norm read W once, and products with N = r
     // (x A^T, dh B) read their long operand once
-    {128, 384, GEMM_DMA_BK, true, 0.77f, true, true},
+    {128, 384, GEMM_DMA_BK, true, 0.77f, true, true, true},
     // 4 waves (4 x 1): the same with M = r (Q^T x)
-    {384, 128, GEMM_DMA_BK, true, 0.77f, true, false},
+    {384, 128, GEMM_DMA_BK, true, 0.77f, true, false, false},
 };
 
 }  // namespace
