@@ -14,7 +14,12 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdora.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "dora_api.cpp"]
+# (source, extra defines, object name): the pipelined GEMM's tile
+# configurations are one source compiled once per configuration, so that they
+# build in parallel.
+SOURCES = [("gemm_bf16.hip", (), "gemm_bf16"), ("gemm_f32.hip", (), "gemm_f32"),
+           ("elementwise.hip", (), "elementwise"), ("dora_api.cpp", (), "dora_api")] + \
+          [("gemm_dma_cfg.hip", (f"-DDORA_DMA_CFG={k}",), f"gemm_dma_cfg{k}") for k in range(7)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -23,13 +28,14 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}"
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src, extra=()):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(unit, extra=()):
+    src, defines, name = unit
+    obj = os.path.join(BUILD, name + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *defines, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    noise = ("'-packed-fp32-ops' is not a recognized feature for this target",)
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(q in l for q in noise))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
     return obj, err
@@ -37,7 +43,7 @@ def _compile(src, extra=()):
 
 def build(verbose=False, extra=()):
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         results = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     for (obj, err) in results:
         if verbose and err.strip():

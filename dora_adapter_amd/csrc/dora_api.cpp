@@ -90,7 +90,20 @@ bool dma_operand(int64_t rows, int64_t K)
 }
 bool dma_mn_operand(int64_t K, int64_t ld)
 {
-    return (K + GEMM_DMA_BK) * ld * 2 < kDmaBytes;
+    return ld % 8 == 0 && (K + GEMM_DMA_BK) * ld * 2 < kDmaBytes;
+}
+
+// Whether a bf16 product has an operand of ragged width: a K-major operand
+// ([rows][K], ld = K) whose K is not a multiple of 8, or an MN-major one
+// ([K][M or N], ld = M or N) whose M or N is not.  Only the element-masked
+// configuration takes those.
+bool shape_ragged(const GemmShape &sh)
+{
+    const bool ak = sh.layout < 2, bk = sh.layout == 0;
+    for (int q = 0; q < sh.nseg; ++q)
+        if ((ak || bk) && sh.K[q] % 8)
+            return true;
+    return (!ak && sh.M % 8) || (!bk && sh.N % 8);
 }
 
 GemmShape nt_shape(int64_t M, int64_t N, int64_t K)
@@ -124,6 +137,7 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
     double best_cost = -1.0;
     const int ncfg = bf16 ? gemm_bf16_num_cfgs() : 1;
     const int forced = bf16 ? forced_tile_cfg() : -1;
+    const bool ragged = bf16 && shape_ragged(sh);
     // pass 0: the forced configuration only (if any); pass 1: all of them,
     // when pass 0 found none that serves this product
     for (int pass = forced >= 0 ? 0 : 1; pass < 2 && best_cost < 0; ++pass)
@@ -134,7 +148,8 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
             continue;
         if (bf16) {
             const TileCfg t = gemm_bf16_cfg(c);
-            if ((t.dma && !sh.dma_ok) || (!t.store_ok && !sh.rowdot) || (sh.rowsq && !t.rowsq_ok))
+            if ((t.dma && !sh.dma_ok) || (!t.store_ok && !sh.rowdot) || (sh.rowsq && !t.rowsq_ok) ||
+                (ragged && !t.ragged_ok))
                 continue;
             BM = t.BM;
             BN = t.BN;
@@ -437,9 +452,6 @@ int check_dims(int dtype, int64_t T, int64_t d_in, int64_t d_out, int64_t r)
     if (d_in < 1 || d_in > kMaxDim || d_out < 1 || d_out > kMaxDim || r < 1 || r > kMaxDim)
         return fail(DORA_E_SHAPE, "need 1 <= d_in, d_out, r < 2^31 (got %lld, %lld, %lld)",
                     (long long)d_in, (long long)d_out, (long long)r);
-    if (dtype == DORA_BF16 && ((d_in % 8) || (d_out % 8) || (r % 8)))
-        return fail(DORA_E_SHAPE, "bf16 needs d_in, d_out, r multiples of 8 (got %lld, %lld, %lld)",
-                    (long long)d_in, (long long)d_out, (long long)r);
     return DORA_OK;
 }
 
@@ -669,14 +681,32 @@ int forward_impl(const void *x, const void *W, const void *A, const void *B, con
     if (T == 0)
         return DORA_OK;
     void *P = P_out ? P_out : static_cast<void *>(w + p.o_P);
-    // 2. P = x A^T (kept for the backward).
-    DORA_CHECK(run_store(bf, p.p, seg1(T, r, x, d_in, A, d_in, d_in), 0, P, r, 1.0f,
-                         reinterpret_cast<float *>(w + p.o_Ppart), st, "adapter x A^T"));
-    // 3. s P as the second K segment's operand (P itself when s = 1).
-    const void *sP = P;
-    if (s != 1.0f) {
-        DORA_LAUNCH(launch_scale(bf, P, s, T * r, w + p.o_sP, st), "scale s P");
-        sP = w + p.o_sP;
+    // 2. P = x A^T (kept for the backward) and, unless s = 1, s P as the
+    //    second K segment's operand: both from the same fp32 sums, each
+    //    rounded once.
+    void *sP = s != 1.0f ? static_cast<void *>(w + p.o_sP) : P;
+    {
+        GemmArgs g = seg1(T, r, x, d_in, A, d_in, d_in);
+        g.mode = EPI_STORE;
+        if (p.p.splits <= 1) {
+            g.out = P;
+            g.ldc = r;
+            g.out_f32 = bf ? 0 : 1;
+            if (sP != P) {
+                g.out2 = sP;
+                g.alpha2 = s;
+            }
+            DORA_LAUNCH(run_gemm(bf, p.p, g, 0, false, st), "adapter x A^T");
+        } else {
+            float *part = reinterpret_cast<float *>(w + p.o_Ppart);
+            g.out = part;
+            g.ldc = r;
+            g.out_f32 = 1;
+            DORA_LAUNCH(run_gemm(bf, p.p, g, 0, false, st), "adapter x A^T");
+            DORA_LAUNCH(launch_splitk_reduce(bf, part, p.p.splits, T, r, 1.0f, P, st, nullptr,
+                                             nullptr, sP != P ? sP : nullptr, s),
+                        "adapter x A^T reduce");
+        }
     }
     // 4. y = (m/n) (x W^T + s P B^T): one K-concatenated product; the epilogue
     //    applies the magnitude scale in the cancellation-safe form and rounds once.
@@ -1092,10 +1122,8 @@ int forward_group_impl(const void *x, int64_t T, const dora_module *mods, int co
     for (const FwdGroupChunk &c : f.chunks) {
         const int cnt = c.i1 - c.i0;
         GemmGroup gp, gf;
-        ItemGroup<ScaleItem> sc;
         memset(&gp, 0, sizeof gp);
         memset(&gf, 0, sizeof gf);
-        memset(&sc, 0, sizeof sc);
         gp.count = gf.count = cnt;
         std::vector<const void *> sP(cnt);
         for (int k = 0; k < cnt; ++k) {
@@ -1112,10 +1140,11 @@ int forward_group_impl(const void *x, int64_t T, const dora_module *mods, int co
             g.out_f32 = bf ? 0 : 1;
             g.splits = 1;
             g.steps_per_split = c.pp[k].sps;
-            // 3. s P
+            // 3. s P from the same sums (rounded once), unless s = 1
             sP[k] = P;
             if (md.s != 1.0f) {
-                sc.it[sc.count++] = ScaleItem{P, w + c.o_sP[k], md.s, T * r};
+                g.out2 = w + c.o_sP[k];
+                g.alpha2 = md.s;
                 sP[k] = w + c.o_sP[k];
             }
             // 4. y = (m/n) (x W^T + s P B^T)
@@ -1133,7 +1162,6 @@ int forward_group_impl(const void *x, int64_t T, const dora_module *mods, int co
             h.steps_per_split = c.pf[k].sps;
         }
         DORA_LAUNCH(launch_gemm_bf16_grouped(gp, 0, c.p.cfg, false, st), "grouped x A^T");
-        DORA_LAUNCH(launch_scale_grouped(bf, sc, st), "grouped s P");
         DORA_LAUNCH(launch_gemm_bf16_grouped(gf, 0, c.fused.cfg, false, st),
                     "grouped fused forward product");
     }
@@ -1231,8 +1259,6 @@ int dora_compose(const void *base, const void *lora, const float *m, const float
     if (T < 0 || T > kMaxDim || d_out < 0 || d_out > kMaxDim)
         return fail(DORA_E_SHAPE, "T=%lld, d_out=%lld out of range", (long long)T,
                     (long long)d_out);
-    if (dtype == DORA_BF16 && (d_out % 8))
-        return fail(DORA_E_SHAPE, "bf16 needs d_out a multiple of 8 (got %lld)", (long long)d_out);
     const bool any = T > 0 && d_out > 0;  // empty tensors may come with NULL data
     DORA_CHECK(check_ptrs({{base, "base", any}, {lora, "lora", any}, {m, "m", d_out > 0},
                            {n, "n", d_out > 0}, {y, "y", any}}));
@@ -1265,7 +1291,6 @@ int dora_forward(const void *x, const void *W, const void *A, const void *B, con
         return fail(DORA_E_NULL, "U_out needs the norm computed here (n_in must be NULL)");
     const FwdPlan p = plan_forward(T, d_in, d_out, r, dtype);
     DORA_CHECK(check_ws(ws, ws_bytes, p.bytes));
-    const bool bf = dtype == DORA_BF16;
     const size_t e = esize(dtype);
     const Range rx{x, T * d_in * e}, rW{W, d_out * d_in * e}, rA{A, r * d_in * e},
         rB{B, d_out * r * e}, rm{m, d_out * sizeof(float)}, rnin{n_in, d_out * sizeof(float)};

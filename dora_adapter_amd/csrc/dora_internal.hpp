@@ -47,6 +47,11 @@ struct GemmArgs {
     // it (one writer per element: unsplit products only)
     int out_accum;
     float alpha;
+    // EPI_STORE, unsplit only: an optional second output of the same type,
+    // layout and ldc receiving alpha2 * C, rounded once (the forward's P and
+    // s P from one accumulator)
+    void *out2;
+    float alpha2;
     // optional per-column magnitude scale of the store: with colm and coln
     // set, column n of alpha * C is stored as h + ((colm[n] - coln[n]) /
     // coln[n]) h, i.e. (m/n) h in the cancellation-safe form (EPI_MERGE:
@@ -103,6 +108,7 @@ struct TileCfg {
     bool store_ok;    // EPI_STORE supported (else EPI_ROWDOT only)
     bool rowsq_ok;    // row sums of squares of A supported
     bool direct_rowdot;  // EPI_ROWDOT formed from the accumulators (no LDS staging)
+    bool ragged_ok;      // also takes operands of any width (element-masked loads)
 };
 int gemm_bf16_num_cfgs();
 TileCfg gemm_bf16_cfg(int cfg);
@@ -119,9 +125,11 @@ hipError_t launch_compose(int bf16, const void *base, const void *lora, const fl
                           hipStream_t st);
 // out = alpha * sum_z part[z] (fixed order); with colm/coln set, column n is
 // then scaled as h + ((colm[n] - coln[n]) / coln[n]) h before the rounding.
+// With out2 set, out2 = alpha2 * sum_z part[z] as well (one rounding each).
 hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t M, int64_t N,
                                 float alpha, void *out, hipStream_t st,
-                                const float *colm = nullptr, const float *coln = nullptr);
+                                const float *colm = nullptr, const float *coln = nullptr,
+                                void *out2 = nullptr, float alpha2 = 1.0f);
 hipError_t launch_gram_finalize(int bf16, const float *part, int splits, int64_t r, void *G_out,
                                 hipStream_t st);
 hipError_t launch_norm_finish(const float *base_part, int zb, const float *cross_part, int zc,
@@ -163,17 +171,9 @@ struct NormFinishItem {
     float s;
     float *n;
 };
-struct ScaleItem {
-    const void *src;
-    void *dst;
-    float s;
-    int64_t n;
-};
 hipError_t launch_gram_finalize_grouped(int bf16, const ItemGroup<GramItem> &g, hipStream_t st);
 hipError_t launch_norm_finish_grouped(const ItemGroup<NormFinishItem> &g, hipStream_t st);
-hipError_t launch_scale_grouped(int bf16, const ItemGroup<ScaleItem> &g, hipStream_t st);
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st);
-hipError_t launch_scale(int bf16, const void *src, float s, int64_t n, void *dst, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
 
 // dh/dm partial sums: rows of T per chunk and number of chunks.

@@ -7,8 +7,7 @@
 //                backward (DoRA summary, "Statistical analysis"), one pass
 //                over dy and y with fixed-order partial sums.
 //   small ones   split-K reduction, Gram matrix finalisation (fp32 sum of
-//                split partials, bf16 hi/lo split), the row-norm finish, and
-//                the scaled copy s P of the adapter activations.
+//                split partials, bf16 hi/lo split) and the row-norm finish.
 //
 // Streaming layout: a thread owns one group of 8 consecutive columns and a
 // contiguous run of rows, so per-column factors (g - 1, g s) are formed once
@@ -120,13 +119,16 @@ __global__ void __launch_bounds__(EW_THREADS)
     const int64_t t1 = (t0 + rows) < Tn ? (t0 + rows) : Tn;
     const int64_t i0 = c * 8;
     const int cnt = (d_out - i0) < 8 ? static_cast<int>(d_out - i0) : 8;
+    // per-column factors, once per run, each rounded once to fp32 from fp64
+    // (g - 1 = (m - n) / n and g s = m s / n): the lora term then carries two
+    // roundings (g s, its product with lora) instead of three
     float gm1[8], gs[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const float mi = q < cnt ? m[i0 + q] : 1.f;
-        const float ni = q < cnt ? n[i0 + q] : 1.f;
-        gm1[q] = (mi - ni) / ni;  // exact m - n when n/2 <= m <= 2n (Sterbenz)
-        gs[q] = (mi / ni) * s;
+        const double mi = q < cnt ? m[i0 + q] : 1.0;
+        const double ni = q < cnt ? n[i0 + q] : 1.0;
+        gm1[q] = static_cast<float>((mi - ni) / ni);
+        gs[q] = static_cast<float>(mi * static_cast<double>(s) / ni);
     }
     if (VEC) {
         // UNROLL rows per iteration, all loads before any store: y may be
@@ -266,7 +268,8 @@ template <typename T>
 __global__ void splitk_reduce_kernel(const float *__restrict__ part, int splits, int64_t MN,
                                      int64_t N, float alpha, T *__restrict__ out,
                                      const float *__restrict__ colm,
-                                     const float *__restrict__ coln)
+                                     const float *__restrict__ coln, T *__restrict__ out2,
+                                     float alpha2)
 {
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < MN;
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -279,6 +282,8 @@ __global__ void splitk_reduce_kernel(const float *__restrict__ part, int splits,
             v = __fmaf_rn((colm[n] - coln[n]) / coln[n], v, v);
         }
         Vec8<T>::store1(out + e, v);
+        if (out2 != nullptr)
+            Vec8<T>::store1(out2 + e, alpha2 * acc);
     }
 }
 
@@ -455,25 +460,6 @@ __global__ void norm_finish_grouped_kernel(ItemGroup<NormFinishItem> g)
                         nullptr, nullptr);
 }
 
-template <typename T>
-__global__ void scale_kernel(const T *__restrict__ src, float s, int64_t n, T *__restrict__ dst)
-{
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        Vec8<T>::store1(dst + i, s * Vec8<T>::load1(src + i));
-}
-
-template <typename T>
-__global__ void scale_grouped_kernel(ItemGroup<ScaleItem> g)
-{
-    const ScaleItem &it = g.it[blockIdx.y];
-    const T *src = static_cast<const T *>(it.src);
-    T *dst = static_cast<T *>(it.dst);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < it.n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        Vec8<T>::store1(dst + i, it.s * Vec8<T>::load1(src + i));
-}
-
 __global__ void copy_f32_kernel(const float *__restrict__ src, float *__restrict__ dst, int64_t n)
 {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -581,7 +567,7 @@ hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, i
 
 hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t M, int64_t N,
                                 float alpha, void *out, hipStream_t st, const float *colm,
-                                const float *coln)
+                                const float *coln, void *out2, float alpha2)
 {
     const int64_t MN = M * N;
     if (MN == 0)
@@ -592,11 +578,13 @@ hipError_t launch_splitk_reduce(int bf16, const float *part, int splits, int64_t
     if (bf16)
         hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)),
                            dim3(EW_THREADS), 0, st, part, splits, MN, N, alpha,
-                           static_cast<uint16_t *>(out), colm, coln);
+                           static_cast<uint16_t *>(out), colm, coln,
+                           static_cast<uint16_t *>(out2), alpha2);
     else
         hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3(static_cast<unsigned>(blocks)),
                            dim3(EW_THREADS), 0, st, part, splits, MN, N, alpha,
-                           static_cast<float *>(out), colm, coln);
+                           static_cast<float *>(out), colm, coln, static_cast<float *>(out2),
+                           alpha2);
     return hipGetLastError();
 }
 
@@ -715,47 +703,11 @@ hipError_t launch_norm_finish_grouped(const ItemGroup<NormFinishItem> &g, hipStr
     return hipGetLastError();
 }
 
-hipError_t launch_scale_grouped(int bf16, const ItemGroup<ScaleItem> &g, hipStream_t st)
-{
-    int64_t most = 0;
-    for (int k = 0; k < g.count; ++k)
-        most = most > g.it[k].n ? most : g.it[k].n;
-    if (g.count == 0 || most == 0)
-        return hipSuccess;
-    int64_t blocks = (most + EW_THREADS - 1) / EW_THREADS;
-    if (blocks > 4096)
-        blocks = 4096;
-    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(g.count));
-    if (bf16)
-        hipLaunchKernelGGL(scale_grouped_kernel<uint16_t>, grid, dim3(EW_THREADS), 0, st, g);
-    else
-        hipLaunchKernelGGL(scale_grouped_kernel<float>, grid, dim3(EW_THREADS), 0, st, g);
-    return hipGetLastError();
-}
-
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st)
 {
     if (n == 0)
         return hipSuccess;
     hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(n)), dim3(EW_THREADS), 0, st, src, dst, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_scale(int bf16, const void *src, float s, int64_t n, void *dst, hipStream_t st)
-{
-    if (n == 0)
-        return hipSuccess;
-    int64_t blocks = (n + EW_THREADS - 1) / EW_THREADS;
-    if (blocks > 8192)
-        blocks = 8192;
-    if (bf16)
-        hipLaunchKernelGGL((scale_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(EW_THREADS), 0, st, static_cast<const uint16_t *>(src), s, n,
-                           static_cast<uint16_t *>(dst));
-    else
-        hipLaunchKernelGGL((scale_kernel<float>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(EW_THREADS), 0, st, static_cast<const float *>(src), s, n,
-                           static_cast<float *>(dst));
     return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ struct EChunk<uint16_t> {
     uint4 raw;
     __device__ __forceinline__ void load(const uint16_t *p, int cnt)
     {
-        if (cnt == 8) {
+        if (cnt == 8 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
             raw = *reinterpret_cast<const uint4 *>(p);
         } else {
             uint32_t w[4];
@@ -81,6 +81,32 @@ struct EChunk<float> {
     }
     __device__ __forceinline__ float get(int q) const { return v[q]; }
 };
+
+// Store up to 8 consecutive elements v[0 .. cnt) of a row at o, rounded once
+// to the element type: one or two 16-byte stores when all 8 are live and o
+// is 16-byte aligned (rows of a ragged width need not be), else element by
+// element.
+__device__ __forceinline__ void store_row8(uint16_t *o, const float (&v)[8], int cnt)
+{
+    if (cnt == 8 && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+        *reinterpret_cast<uint4 *>(o) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+        for (int q = 0; q < cnt; ++q)
+            o[q] = f32_to_bf16(v[q]);
+    }
+}
+__device__ __forceinline__ void store_row8(float *o, const float (&v)[8], int cnt)
+{
+    if (cnt == 8 && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+        reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        for (int q = 0; q < cnt; ++q)
+            o[q] = v[q];
+    }
+}
 
 // Process rows [mrow0, mrow0 + R) of the tile whose first column is n0.
 // Every thread of the workgroup must call this (row-dot uses wave shuffles).
@@ -133,27 +159,21 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
                 if (g.out_accum) {
                     for (int q = 0; q < cnt; ++q)
                         o[q] += v[q];
-                } else if (cnt == 8 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
-                    reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
-                    reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
                 } else {
-                    for (int q = 0; q < cnt; ++q)
-                        o[q] = v[q];
-                }
-            } else if constexpr (sizeof(TE) == 2) {
-                uint16_t *o = static_cast<uint16_t *>(g.out) + m * g.ldc + n;
-                if (cnt == 8) {
-                    *reinterpret_cast<uint4 *>(o) =
-                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-                } else {
-                    for (int q = 0; q < cnt; ++q)
-                        o[q] = f32_to_bf16(v[q]);
+                    store_row8(o, v, cnt);
                 }
             } else {
-                float *o = static_cast<float *>(g.out) + m * g.ldc + n;
-                for (int q = 0; q < cnt; ++q)
-                    o[q] = v[q];
+                store_row8(static_cast<TE *>(g.out) + m * g.ldc + n, v, cnt);
+            }
+            if (g.out2 != nullptr) {
+                // the second output: alpha2 * C, rounded once
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    v[q] = g.alpha2 * Cs[row * CST + c * 8 + q];
+                if (g.out_f32)
+                    store_row8(static_cast<float *>(g.out2) + m * g.ldc + n, v, cnt);
+                else
+                    store_row8(static_cast<TE *>(g.out2) + m * g.ldc + n, v, cnt);
             }
         }
     } else if (g.mode == EPI_MERGE) {
@@ -189,21 +209,7 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
                 const float w = e[it].get(q);
                 v[q] = w + __fmaf_rn(gm1[it], w, gs[it] * Cs[row * CST + c * 8 + q]);
             }
-            if constexpr (sizeof(TE) == 2) {
-                uint16_t *o = static_cast<uint16_t *>(g.out) + m * g.ldc + n;
-                if (cnt == 8) {
-                    *reinterpret_cast<uint4 *>(o) =
-                        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-                } else {
-                    for (int q = 0; q < cnt; ++q)
-                        o[q] = f32_to_bf16(v[q]);
-                }
-            } else {
-                float *o = static_cast<float *>(g.out) + m * g.ldc + n;
-                for (int q = 0; q < cnt; ++q)
-                    o[q] = v[q];
-            }
+            store_row8(static_cast<TE *>(g.out) + m * g.ldc + n, v, cnt);
         }
     } else {  // EPI_ROWDOT
         const int ntn = static_cast<int>((N + BN - 1) / BN);

@@ -28,7 +28,7 @@
 //   * XCD-aware tile order (epilogue.hpp, tile_coords).
 #include "dora_internal.hpp"
 #include "epilogue.hpp"
-#include "gemm_bf16_dma.hpp"
+#include "gemm_dma_launch.hpp"
 
 namespace dora {
 namespace {
@@ -47,13 +47,54 @@ struct OpRegs {
     static constexpr int PER = KMAJ ? (R * 8) / NT : ((R + NT - 1) / NT) * 8;
 };
 
-template <bool KMAJ, int R, int NT, int NV>
+// Eight consecutive bf16 values p[0 .. 8) with those at or past `live`
+// read as zero, loaded one by one (for rows of a ragged width, which need
+// not be 16-byte aligned).
+__device__ __forceinline__ uint4 load8_masked(const uint16_t *__restrict__ p, int64_t live)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = 2 * q < live ? p[2 * q] : 0u;
+        const uint32_t hi = 2 * q + 1 < live ? p[2 * q + 1] : 0u;
+        w[q] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// RG (ragged): any K, M, N and leading dimension; every element is loaded
+// on its own and masked.  Otherwise K-major operands need K and ld
+// multiples of 8, MN-major ones M (or N) and ld multiples of 8, so that
+// every 16-byte chunk is aligned and wholly in or wholly out.
+template <bool KMAJ, int R, int NT, bool RG, int NV>
 __device__ __forceinline__ void load_operand(uint4 (&v)[NV], const uint16_t *__restrict__ p,
                                              int64_t ld, int64_t MN, int64_t K, int64_t mn0,
                                              int64_t k0, int tid)
 {
     static_assert(NV == OpRegs<KMAJ, R, NT>::PER, "register count");
-    if constexpr (KMAJ) {
+    if constexpr (RG && KMAJ) {
+#pragma unroll
+        for (int i = 0; i < OpRegs<KMAJ, R, NT>::PER; ++i) {
+            const int idx = tid + i * NT;
+            const int row = idx >> 3, c = idx & 7;
+            const int64_t mn = mn0 + row, k = k0 + c * 8;
+            v[i] = mn < MN && k < K ? load8_masked(p + mn * ld + k, K - k)
+                                    : make_uint4(0, 0, 0, 0);
+        }
+    } else if constexpr (RG) {
+#pragma unroll
+        for (int b = 0; b < OpRegs<KMAJ, R, NT>::PER / 8; ++b) {
+            const int idx = tid + b * NT;
+            const int kb = idx / (R / 8), mb = idx % (R / 8);
+            const int64_t mn = mn0 + mb * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t k = k0 + kb * 8 + j;
+                v[b * 8 + j] = idx < R && mn < MN && k < K ? load8_masked(p + k * ld + mn, MN - mn)
+                                                           : make_uint4(0, 0, 0, 0);
+            }
+        }
+    } else if constexpr (KMAJ) {
         static_assert((R * 8) % NT == 0, "K-major tile must split evenly");
 #pragma unroll
         for (int i = 0; i < OpRegs<KMAJ, R, NT>::PER; ++i) {
@@ -151,7 +192,7 @@ struct Smem {
     static constexpr int BYTES = OPS > EPI ? OPS : EPI;
 };
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ, bool RG>
 __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
 {
     using SM = Smem<BM, BN, WM, WN>;
@@ -200,10 +241,10 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
         const bool first = s < st1;
         const GemmSeg &sg = first ? g.seg[0] : g.seg[1];
         const int64_t k0 = (first ? s : s - st1) * BK;
-        load_operand<AK, BM, NT>(ra, static_cast<const uint16_t *>(sg.a), sg.lda, g.M, sg.K, m0,
-                                 k0, tid);
-        load_operand<BKM, BN, NT>(rb, static_cast<const uint16_t *>(sg.b), sg.ldb, g.N, sg.K, n0,
-                                  k0, tid);
+        load_operand<AK, BM, NT, RG>(ra, static_cast<const uint16_t *>(sg.a), sg.lda, g.M, sg.K,
+                                     m0, k0, tid);
+        load_operand<BKM, BN, NT, RG>(rb, static_cast<const uint16_t *>(sg.b), sg.ldb, g.N, sg.K,
+                                      n0, k0, tid);
     };
     auto store_step = [&](int buf) {
         if constexpr (ROWSQ) {
@@ -307,154 +348,72 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
 // for the square ones, and, for 128 x 128 and the rank-wide tiles, the
 // rate they reach as one wave of tiles on the rank-r products (x A^T,
 // dh^T P, Q^T x at the training shape).
+// The 128 x 128 register-staged configuration also exists with
+// element-masked loads (ragged_ok), for operands of any width.
 constexpr TileCfg kCfgs[] = {
-    {256, 256, GEMM_BK, false, 0.76f, true, true, false},
-    {256, 128, GEMM_BK, false, 0.68f, true, true, false},
-    {128, 128, GEMM_BK, false, 0.56f, true, true, false},
-    {128, 64, GEMM_BK, false, 0.40f, true, true, false},
-    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false, false},  // 4 waves (2 x 2), 128 x 128 per wave
-    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false, false},  // 4 waves (2 x 2)
-    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false, false},  // 4 waves (2 x 2), 2 per CU
+    {256, 256, GEMM_BK, false, 0.76f, true, true, false, false},
+    {256, 128, GEMM_BK, false, 0.68f, true, true, false, false},
+    {128, 128, GEMM_BK, false, 0.56f, true, true, false, true},
+    {128, 64, GEMM_BK, false, 0.40f, true, true, false, false},
+    // 4 waves (2 x 2), 128 x 128 per wave
+    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false, false, false},
+    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false, false, false},  // 4 waves (2 x 2)
+    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false, false, false},  // 4 waves (2 x 2), 2 per CU
     // 4 waves (1 x 4): a whole rank-384 row block per tile, so the row-dot
     // products of the factored norm read W once, and products with N = r
     // (x A^T, dh B) read their long operand once
-    {128, 384, GEMM_DMA_BK, true, 0.77f, true, true, true},
+    {128, 384, GEMM_DMA_BK, true, 0.77f, true, true, true, false},
     // 4 waves (4 x 1): the same with M = r (Q^T x)
-    {384, 128, GEMM_DMA_BK, true, 0.77f, true, false, false},
+    {384, 128, GEMM_DMA_BK, true, 0.77f, true, false, false, false},
 };
 
 }  // namespace
 
-// Explicit instantiations of the pipelined kernels: with implicit
-// instantiation from the launchers alone, the host compiler emitted launch
-// stubs for only some of them.
-#define DORA_DMA_INST(BM, BN, WM, WN)                                                          \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, true, false>(GemmArgs); \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, true, false, false>(         \
-        GemmArgs);                                                                                \
-    template __global__ void dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, false, false, false>(        \
-        GemmArgs);
-DORA_DMA_INST(256, 256, 2, 2)
-DORA_DMA_INST(256, 128, 2, 2)
-DORA_DMA_INST(128, 128, 2, 2)
-DORA_DMA_INST(128, 384, 1, 4)
-DORA_DMA_INST(384, 128, 4, 1)
-template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 1, 4, true, true, true>(GemmArgs);
-#undef DORA_DMA_INST
-#define DORA_DMA_GROUP_INST(BM, BN, WM, WN)                                                      \
-    template __global__ void dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, true, true, false>( \
-        GemmGroup);                                                                              \
-    template __global__ void dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, true, false, false>( \
-        GemmGroup);
-DORA_DMA_GROUP_INST(256, 256, 2, 2)
-DORA_DMA_GROUP_INST(256, 128, 2, 2)
-DORA_DMA_GROUP_INST(128, 128, 2, 2)
-DORA_DMA_GROUP_INST(128, 384, 1, 4)
-DORA_DMA_GROUP_INST(384, 128, 4, 1)
-template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 1, 4, true, true, true>(
-    GemmGroup);
-#undef DORA_DMA_GROUP_INST
-
 namespace {
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
-hipError_t launch_dma(const GemmArgs &a, hipStream_t st)
-{
-    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    if (tiles == 0 || a.splits == 0)
-        return hipSuccess;
-    dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
-    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, AK, BKM, RS>), grid,
-                       dim3(WM * WN * 64), 0, st, a);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStream_t st)
-{
-    switch (layout) {
-    case 0:
-        if (rowsq) {
-            if constexpr (WM == 1)
-                return launch_dma<BM, BN, WM, WN, true, true, true>(a, st);
-            else
-                return hipErrorInvalidValue;
-        }
-        return launch_dma<BM, BN, WM, WN, true, true, false>(a, st);
-    case 1:
-        return launch_dma<BM, BN, WM, WN, true, false, false>(a, st);
-    case 2:
-        return launch_dma<BM, BN, WM, WN, false, false, false>(a, st);
-    default:
-        return hipErrorInvalidValue;
-    }
-}
-
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
-hipError_t launch_dma_group(GemmGroup &g, hipStream_t st)
-{
-    int64_t total = 0;
-    for (int p = 0; p < g.count; ++p) {
-        g.tile_start[p] = static_cast<int>(total);
-        const GemmArgs &a = g.p[p];
-        total += ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splits;
-    }
-    g.tile_start[g.count] = static_cast<int>(total);
-    if (total == 0)
-        return hipSuccess;
-    if (total > INT32_MAX)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, AK, BKM, RS>),
-                       dim3(static_cast<unsigned>(total)), dim3(WM * WN * 64), 0, st, g);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_dma_group_layout(GemmGroup &g, int layout, bool rowsq, hipStream_t st)
-{
-    switch (layout) {
-    case 0:
-        if (rowsq) {
-            if constexpr (WM == 1)
-                return launch_dma_group<BM, BN, WM, WN, true, true, true>(g, st);
-            else
-                return hipErrorInvalidValue;
-        }
-        return launch_dma_group<BM, BN, WM, WN, true, true, false>(g, st);
-    case 1:
-        if (rowsq)
-            return hipErrorInvalidValue;
-        return launch_dma_group<BM, BN, WM, WN, true, false, false>(g, st);
-    default:
-        return hipErrorInvalidValue;
-    }
-}
-
-template <int BM, int BN, bool AK, bool BKM, bool RS>
+template <int BM, int BN, bool AK, bool BKM, bool RS, bool RG>
 hipError_t launch_one(const GemmArgs &a, hipStream_t st)
 {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles == 0 || a.splits == 0)
         return hipSuccess;
     dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 2, 2, AK, BKM, RS>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 2, 2, AK, BKM, RS, RG>), grid, dim3(256), 0, st,
+                       a);
     return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool RG = false>
 hipError_t launch_cfg(const GemmArgs &a, int layout, bool rowsq, hipStream_t st)
 {
     switch (layout) {
     case 0:
-        return rowsq ? launch_one<BM, BN, true, true, true>(a, st)
-                     : launch_one<BM, BN, true, true, false>(a, st);
+        return rowsq ? launch_one<BM, BN, true, true, true, RG>(a, st)
+                     : launch_one<BM, BN, true, true, false, RG>(a, st);
     case 1:
-        return launch_one<BM, BN, true, false, false>(a, st);
+        return launch_one<BM, BN, true, false, false, RG>(a, st);
     case 2:
-        return launch_one<BM, BN, false, false, false>(a, st);
+        return launch_one<BM, BN, false, false, false, RG>(a, st);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+// Whether a product needs the element-masked loads: a leading dimension or
+// base address that leaves rows unaligned to 16 bytes, a K-major operand
+// whose K is not a multiple of 8, or an MN-major one whose M (or N) is not.
+bool ragged_args(const GemmArgs &a, int layout)
+{
+    const bool ak = layout < 2, bk = layout == 0;
+    for (int q = 0; q < a.nseg; ++q) {
+        const GemmSeg &sg = a.seg[q];
+        if ((sg.lda % 8) || (sg.ldb % 8) || (reinterpret_cast<uintptr_t>(sg.a) & 15) ||
+            (reinterpret_cast<uintptr_t>(sg.b) & 15))
+            return true;
+        if ((ak && sg.K % 8) || (bk && sg.K % 8) || (!ak && a.M % 8) || (!bk && a.N % 8))
+            return true;
+    }
+    return false;
 }
 
 }  // namespace
@@ -476,6 +435,12 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
     if (cfg < 0 || cfg >= gemm_bf16_num_cfgs() || (a.mode != EPI_ROWDOT && !kCfgs[cfg].store_ok) ||
         (rowsq && !kCfgs[cfg].rowsq_ok))
         return hipErrorInvalidValue;
+    if (ragged_args(a, layout)) {
+        // only the element-masked configuration takes unaligned operands
+        if (!kCfgs[cfg].ragged_ok)
+            return hipErrorInvalidValue;
+        return launch_cfg<128, 128, true>(a, layout, rowsq, st);
+    }
     switch (cfg) {
     case 0:
         return launch_cfg<256, 256>(a, layout, rowsq, st);
@@ -486,15 +451,15 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
     case 3:
         return launch_cfg<128, 64>(a, layout, rowsq, st);
     case 4:
-        return launch_dma_layout<256, 256, 2, 2>(a, layout, rowsq, st);
+        return launch_dma_256x256(a, layout, rowsq, st);
     case 5:
-        return launch_dma_layout<256, 128, 2, 2>(a, layout, rowsq, st);
+        return launch_dma_256x128(a, layout, rowsq, st);
     case 6:
-        return launch_dma_layout<128, 128, 2, 2>(a, layout, rowsq, st);
+        return launch_dma_128x128(a, layout, rowsq, st);
     case 7:
-        return launch_dma_layout<128, 384, 1, 4>(a, layout, rowsq, st);
+        return launch_dma_128x384(a, layout, rowsq, st);
     case 8:
-        return launch_dma_layout<384, 128, 4, 1>(a, layout, rowsq, st);
+        return launch_dma_384x128(a, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -510,15 +475,15 @@ hipError_t launch_gemm_bf16_grouped(GemmGroup &g, int layout, int cfg, bool rows
             return hipErrorInvalidValue;
     switch (cfg) {
     case 4:
-        return launch_dma_group_layout<256, 256, 2, 2>(g, layout, rowsq, st);
+        return launch_dma_group_256x256(g, layout, rowsq, st);
     case 5:
-        return launch_dma_group_layout<256, 128, 2, 2>(g, layout, rowsq, st);
+        return launch_dma_group_256x128(g, layout, rowsq, st);
     case 6:
-        return launch_dma_group_layout<128, 128, 2, 2>(g, layout, rowsq, st);
+        return launch_dma_group_128x128(g, layout, rowsq, st);
     case 7:
-        return launch_dma_group_layout<128, 384, 1, 4>(g, layout, rowsq, st);
+        return launch_dma_group_128x384(g, layout, rowsq, st);
     case 8:
-        return launch_dma_group_layout<384, 128, 4, 1>(g, layout, rowsq, st);
+        return launch_dma_group_384x128(g, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -627,19 +627,21 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             static_assert((BM * CPRow) % NT == 0, "E tile chunks must split over threads");
             const uint16_t *E = static_cast<const uint16_t *>(g.E);
             // all loads first, so their latencies overlap
-            uint4 ev[NCH];
+            EChunk<uint16_t> ev[NCH];
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
                 const int idx = tid + k * NT;
                 const int64_t row = m0 + idx / CPRow, col = n0 + (idx % CPRow) * 8;
-                ev[k] = make_uint4(0u, 0u, 0u, 0u);
                 if (row < g.M && col < g.N)
-                    ev[k] = *reinterpret_cast<const uint4 *>(E + row * g.lde + col);
+                    ev[k].load(E + row * g.lde + col, g.N - col < 8 ? static_cast<int>(g.N - col) : 8);
+                else
+                    ev[k].zero();
             }
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
                 const int idx = tid + k * NT;
-                *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) = ev[k];
+                *reinterpret_cast<uint4 *>(smem + (idx / CPRow) * C::EP + (idx % CPRow) * 16) =
+                    ev[k].raw;
             }
             __syncthreads();
             if (g.out != nullptr) {

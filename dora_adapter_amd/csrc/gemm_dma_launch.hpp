@@ -1,0 +1,100 @@
+// gemm_dma_launch.hpp - launchers of the pipelined bf16 GEMM (gemm_bf16_dma.hpp),
+// one set per tile configuration.  Each configuration's kernels are
+// instantiated in their own translation unit (gemm_dma_cfg.hip, compiled once
+// per configuration), so that the configurations compile in parallel.
+#pragma once
+
+#include "gemm_bf16_dma.hpp"
+
+namespace dora {
+namespace dma {
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
+hipError_t launch_dma(const GemmArgs &a, hipStream_t st)
+{
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    if (tiles == 0 || a.splits == 0)
+        return hipSuccess;
+    dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, AK, BKM, RS>), grid,
+                       dim3(WM * WN * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStream_t st)
+{
+    switch (layout) {
+    case 0:
+        if (rowsq) {
+            if constexpr (WM == 1)
+                return launch_dma<BM, BN, WM, WN, true, true, true>(a, st);
+            else
+                return hipErrorInvalidValue;
+        }
+        return launch_dma<BM, BN, WM, WN, true, true, false>(a, st);
+    case 1:
+        return launch_dma<BM, BN, WM, WN, true, false, false>(a, st);
+    case 2:
+        return launch_dma<BM, BN, WM, WN, false, false, false>(a, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
+hipError_t launch_dma_group(GemmGroup &g, hipStream_t st)
+{
+    int64_t total = 0;
+    for (int p = 0; p < g.count; ++p) {
+        g.tile_start[p] = static_cast<int>(total);
+        const GemmArgs &a = g.p[p];
+        total += ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splits;
+    }
+    g.tile_start[g.count] = static_cast<int>(total);
+    if (total == 0)
+        return hipSuccess;
+    if (total > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_grouped_kernel<BM, BN, WM, WN, AK, BKM, RS>),
+                       dim3(static_cast<unsigned>(total)), dim3(WM * WN * 64), 0, st, g);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_dma_group_layout(GemmGroup &g, int layout, bool rowsq, hipStream_t st)
+{
+    switch (layout) {
+    case 0:
+        if (rowsq) {
+            if constexpr (WM == 1)
+                return launch_dma_group<BM, BN, WM, WN, true, true, true>(g, st);
+            else
+                return hipErrorInvalidValue;
+        }
+        return launch_dma_group<BM, BN, WM, WN, true, true, false>(g, st);
+    case 1:
+        if (rowsq)
+            return hipErrorInvalidValue;
+        return launch_dma_group<BM, BN, WM, WN, true, false, false>(g, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+
+}  // namespace dma
+
+// Per-configuration entry points (layout as in launch_gemm_bf16).
+#define DORA_DMA_LAUNCHERS(BM, BN)                                                            \
+    hipError_t launch_dma_##BM##x##BN(const GemmArgs &a, int layout, bool rowsq,                \
+                                      hipStream_t st);                                          \
+    hipError_t launch_dma_group_##BM##x##BN(GemmGroup &g, int layout, bool rowsq, hipStream_t st);
+DORA_DMA_LAUNCHERS(256, 256)
+DORA_DMA_LAUNCHERS(256, 128)
+DORA_DMA_LAUNCHERS(128, 128)
+DORA_DMA_LAUNCHERS(128, 384)
+DORA_DMA_LAUNCHERS(384, 128)
+#undef DORA_DMA_LAUNCHERS
+
+}  // namespace dora

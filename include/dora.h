@@ -34,10 +34,11 @@
  *     validated on the host before anything is enqueued; kernels then run
  *     asynchronously on `stream` and results are valid once it is
  *     synchronised.  Nothing inside synchronises the host.
- *   - Every pointer must be 16-byte aligned.  For DORA_BF16, d_in, d_out
- *     and r must be multiples of 8 (rows of 16 bytes); T may be any value
- *     >= 0.  For DORA_F32 there is no multiple-of-8 requirement.  r >= 1
- *     and d_in >= 1 always.
+ *   - Every pointer must be 16-byte aligned.  Sizes need not be multiples
+ *     of anything: T >= 0, and d_in, d_out, r >= 1 (all < 2^31).  Tails are
+ *     masked in the kernels; a bf16 width that leaves rows unaligned to 16
+ *     bytes (not a multiple of 8) runs on element-masked loads, slower than
+ *     the pipelined path but with the same arithmetic.
  *   - Results are bitwise deterministic for identical inputs: there are no
  *     floating-point atomics and every reduction runs in a fixed order.
  *   - Arithmetic: products accumulate in fp32; matrix outputs are rounded
@@ -64,7 +65,7 @@ extern "C" {
 typedef enum {
     DORA_OK = 0,
     DORA_E_NULL = 1,      /* a required pointer is NULL                      */
-    DORA_E_SHAPE = 2,     /* a size is out of range or breaks a multiple-of-8 rule */
+    DORA_E_SHAPE = 2,     /* a size is out of range                          */
     DORA_E_DTYPE = 3,     /* unknown dora_dtype                              */
     DORA_E_ALIGN = 4,     /* a pointer is not 16-byte aligned                */
     DORA_E_WORKSPACE = 5, /* ws is NULL or ws_bytes is below the query       */
@@ -118,9 +119,9 @@ int dora_factored_norm(const void *W, const void *A, const void *B, float s,
  * dora_compose - the single-pass composition ([SD] abstract, fused
  * compose with a numerically stable form for the near-unity regime):
  *     y[t,i] = base[t,i] + ( (g_i - 1) * base[t,i] + g_i * s * lora[t,i] )
- * with g_i - 1 formed as (m_i - n_i) / n_i and g_i = m_i / n_i in fp32, the
- * bracket summed before base is added, and one rounding to `dtype` at the
- * end.  Mathematically y = (m/n) (.) (base + s*lora).
+ * with g_i - 1 = (m_i - n_i) / n_i and g_i s = m_i s / n_i each rounded once
+ * to fp32, the bracket summed in fp32 before base is added, and one rounding
+ * to `dtype` at the end.  Mathematically y = (m/n) (.) (base + s*lora).
  *   base, lora, y [T, d_out] in `dtype`; m, n [d_out] fp32.
  *   y may be the same pointer as base (in place); any other overlap of y
  *   with base or lora is DORA_E_ALIAS.
@@ -138,9 +139,9 @@ int dora_compose(const void *base, const void *lora, const float *m, const float
  *                                            product's epilogue, rounded once
  *   The base and adapter products share one accumulator, so the composition
  *   happens in the same pass that produces them ([SD]'s single-pass compose,
- *   taken one step further): no [T, d_out] intermediate exists.  s P is
- *   rounded to the element type before the product (exact when s = 1 or a
- *   power of two).
+ *   taken one step further): no [T, d_out] intermediate exists.  P and s P
+ *   are each rounded once to the element type from the same fp32 sums of
+ *   x A^T (s P is P itself when s = 1).
  *   x [T, d_in], W [d_out, d_in], A [r, d_in], B [d_out, r] in `dtype`;
  *   m [d_out] fp32.  y [T, d_out] in `dtype` (output).
  *   n_out [d_out] fp32: receives n (required; with n_in it receives a copy).

@@ -1,6 +1,13 @@
 """GPU parity: dora_compose (stable single-pass form) vs the oracle's plain
 y = (m/n)(base + s*lora), including the near-unity regime where g = m/n is
-within 1e-6 .. 1e-2 of one."""
+within 1e-6 .. 1e-2 of one.
+
+A thread of the compose kernel streams one 8-column group down a run of
+consecutive rows, four rows at a time with a row-by-row tail; the run length
+grows with T * d_out.  The large cases below give runs of 5, 9 and 29 rows
+(the last at the benchmarked 8192 x 28672 output, with a shorter last run),
+so both the four-row blocks and the tail are compared, in place and out of
+place."""
 import numpy as np
 import pytest
 import torch
@@ -27,9 +34,12 @@ def _inputs(T, d_out, dtype, seed, delta=None):
 def _check(y, base, lora, m, n, s, dtype, what):
     ref = O.compose(base, lora, m, n, s)
     got = np64(y)
-    # An fp32 evaluation of the stable form errs by a few fp32 ulps of the
-    # operand magnitudes |base| + |g s lora| (not of |y|: base and s*lora may
-    # cancel); bf16 output adds at most one bf16 ulp of rounding.
+    # The kernel evaluates y = b + fma(g - 1, b, (g s) l) with g - 1 and g s
+    # each rounded once to fp32, then (g s) l, the fma and the final add: with
+    # u = 2^-24, |err| <= u |y| + u |(g-1) b + g s l| + u |g-1| |b| + 2u |g s l|
+    # <= u |b| (1 + 3 |g-1|) + 4u |g s l| <= 4u (|b| + |g s l|) for |g-1| <= 1,
+    # a bound in the operand magnitudes (not |y|: base and s lora may cancel);
+    # bf16 output adds at most one bf16 ulp of rounding.
     g = np64(m) / np64(n)
     operand = np.abs(np64(base)) + np.abs(g * s * np64(lora))
     err = np.abs(got - ref)
@@ -45,6 +55,7 @@ def _check(y, base, lora, m, n, s, dtype, what):
 
 @pytest.mark.parametrize("T,d_out,dtype", [
     (37, 200, torch.bfloat16), (1000, 4096, torch.bfloat16), (3, 8, torch.bfloat16),
+    (37, 201, torch.bfloat16), (5, 3, torch.bfloat16),  # ragged widths: element by element
     (16, 64, torch.float32), (33, 60, torch.float32), (129, 1000, torch.float32),
 ])
 def test_compose_matches_oracle(T, d_out, dtype):
@@ -98,3 +109,50 @@ def test_compose_deterministic():
     b = D.dora_compose(gpu(base), gpu(lora), gpu(m), gpu(n), 1.0)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def _run_length(T, d_out, target=2 * 256 * 8 * 64 * 4):
+    """Rows per thread run of the compose launch (it aims for 2^20 threads)."""
+    gpr = (d_out + 7) // 8
+    runs = max(min(target // gpr, T), 1)
+    return -(-T // runs)
+
+
+@pytest.mark.parametrize("T,d_out,dtype,rows", [
+    (4100, 8192, torch.bfloat16, 5),      # one four-row block and a one-row tail
+    (4100, 16384, torch.float32, 9),      # two blocks and a tail, fp32
+])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_compose_unrolled_runs_full(T, d_out, dtype, rows, in_place):
+    assert _run_length(T, d_out) == rows
+    say("compose unrolled runs", T, d_out, dtype, "in place" if in_place else "out of place")
+    base, lora, m, n = _inputs(T, d_out, dtype, seed=T + d_out + in_place)
+    s = 0.75
+    gb = gpu(base)
+    y = D.dora_compose(gb, gpu(lora), gpu(m), gpu(n), s, y=gb if in_place else None)
+    torch.cuda.synchronize()
+    assert (y.data_ptr() == gb.data_ptr()) == in_place
+    _check(y.cpu(), base, lora, m, n, s, dtype, f"compose {T}x{d_out}")
+
+
+@pytest.mark.parametrize("T", [8192, 8191])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_compose_benchmark_shape_rows(T, in_place):
+    """The benchmarked output, 8192 x 28672 bf16 (runs of 29 rows: seven
+    four-row blocks and a tail; the last run shorter), and 8191 rows.  Every
+    column of the first 64 rows, the last 64 rows and 64 sampled rows is
+    compared with the oracle."""
+    d_out, dtype = 28672, torch.bfloat16
+    assert _run_length(T, d_out) == 29
+    say("compose benchmark shape", T, d_out, "in place" if in_place else "out of place")
+    base, lora, m, n = _inputs(T, d_out, dtype, seed=T + in_place)
+    s = 1.0
+    gb = gpu(base)
+    y = D.dora_compose(gb, gpu(lora), gpu(m), gpu(n), s, y=gb if in_place else None)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(T)
+    rows = sorted(set(range(64)) | set(range(T - 64, T)) |
+                  set(torch.randint(64, T - 64, (64,), generator=g).tolist()))
+    idx = torch.tensor(rows)
+    _check(y[idx.to(y.device)].cpu(), base[idx], lora[idx], m, n, s, dtype,
+           f"compose {T}x{d_out} sampled rows")

@@ -3,8 +3,9 @@
 Full comparisons at sizes the oracle finishes in seconds (several tiles,
 ragged token counts), the tiny fp32 module, the invariants (B = 0 with
 m = n returns the base product; m = n returns plain LoRA; a cached norm
-reproduces the recomputed one bit for bit), and the full module shapes on
-sampled (token, row) entries."""
+reproduces the recomputed one bit for bit; B = 0 with m = n is dora_linear's
+x W^T bit for bit), and the full module shapes on sampled (token, row)
+entries."""
 import numpy as np
 import pytest
 import torch
@@ -74,6 +75,29 @@ def test_invariant_b_zero_m_equals_n():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     check_close(y1, np64(mod["x"]) @ np64(mod["W"]).T, torch.bfloat16, "y = x W^T")
+
+
+@pytest.mark.parametrize("s", [1.0, 0.5])
+def test_b_zero_is_bitwise_the_base_product(s):
+    """B = 0 and m = dora_factored_norm(W, A, 0, s): (m - n) / n is exactly 0
+    and the adapter segment adds exact zeros to the fp32 accumulator, so
+    dora_forward returns dora_linear's x W^T bit for bit.  The shape is one
+    where neither product is split over K (asserted through the workspace
+    queries), so both accumulate the same K steps in the same order."""
+    T, d_out, d_in, r = 4096, 4096, 1024, 64
+    say("forward B=0 bitwise vs dora_linear", T, d_out, d_in, r, s)
+    L = D.lib()
+    assert D.dora_linear_workspace(T, d_in, d_out, D.DORA_BF16) == 0
+    mod = synth.custom(d_out, d_in, r, T, "bf16", s, seed=25)
+    W, A, x = gpu(mod["W"]), gpu(mod["A"]), gpu(mod["x"])
+    B0 = torch.zeros(d_out, r, dtype=torch.bfloat16, device="cuda:0")
+    n = D.dora_factored_norm(W, A, B0, s)
+    y, _, _ = D.dora_forward(x, W, A, B0, n, s)
+    base = D.dora_linear(x, W)
+    torch.cuda.synchronize()
+    assert L.dora_last_error() == b""
+    assert torch.equal(y, base), f"{int((y != base).sum())} elements differ from x W^T"
+    check_close(y, np64(mod["x"]) @ np64(mod["W"]).T, torch.bfloat16, "y = x W^T")
 
 
 def test_lora_reduction_and_cached_norm():
