@@ -18,7 +18,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 # configurations are one source compiled once per configuration, so that they
 # build in parallel.
 SOURCES = [("gemm_bf16.hip", (), "gemm_bf16"), ("gemm_f32.hip", (), "gemm_f32"),
-           ("elementwise.hip", (), "elementwise"), ("dora_api.cpp", (), "dora_api")] + \
+           ("elementwise.hip", (), "elementwise"), ("dora_api.cpp", (), "dora_api"),
+           ("noalloc.hip", (), "noalloc")] + \
           [("gemm_dma_cfg.hip", (f"-DDORA_DMA_CFG={k}",), f"gemm_dma_cfg{k}") for k in range(7)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -36,6 +36,21 @@ int hip_fail(hipError_t e, const char *what)
     return fail(DORA_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+int set_error(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+namespace {
+
 #define DORA_LAUNCH(expr, what)                      \
     do {                                             \
         hipError_t e_ = (expr);                      \

@@ -176,6 +176,11 @@ hipError_t launch_norm_finish_grouped(const ItemGroup<NormFinishItem> &g, hipStr
 hipError_t launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t st);
 hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
 
+// The thread-local message dora_last_error() returns (dora_api.cpp): set it
+// and return `status`, or clear it.
+int set_error(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
 // dh/dm partial sums: rows of T per chunk and number of chunks.
 int64_t dm_t_chunk(int64_t T, int64_t d_out);
 

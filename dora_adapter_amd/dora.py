@@ -24,7 +24,7 @@ EXPORTS = ("dora_strerror", "dora_last_error", "dora_norm_workspace", "dora_forw
            "dora_backward", "dora_linear_workspace", "dora_linear", "dora_merge_workspace",
            "dora_merge", "dora_backward_through_norm_workspace", "dora_backward_through_norm",
            "dora_factored_norm_grouped_workspace", "dora_factored_norm_grouped",
-           "dora_forward_grouped_workspace", "dora_forward_grouped")
+           "dora_forward_grouped_workspace", "dora_forward_grouped", "dora_forward_noalloc")
 
 _lib = None
 
@@ -90,6 +90,9 @@ def lib():
         L.dora_linear_workspace.argtypes = [i64, i64, i64, c_int]
         L.dora_linear.restype = c_int
         L.dora_linear.argtypes = [p, p, i64, i64, i64, c_int, p, p, sz, p]
+        L.dora_forward_noalloc.restype = c_int
+        L.dora_forward_noalloc.argtypes = [p, p, p, p, p, f, i64, i64, i64, i64, c_int, p, p, p,
+                                           p, p, p]
         L.dora_merge_workspace.restype = sz
         L.dora_merge_workspace.argtypes = [i64, i64, i64, c_int]
         L.dora_merge.restype = c_int
@@ -199,6 +202,25 @@ def dora_forward(x, W, A, B, m, s, n_in=None, want_P=True, ws=None, y=None, n_ou
     _check(lib().dora_forward(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), float(s), T, d_in,
                               d_out, r, dt, _ptr(y), _ptr(n_out), _ptr(P_out if want_P else None),
                               _ptr(n_in), _ptr(U_out), _ptr(ws), ws.numel(), _stream(dev)))
+    return y, n_out, (P_out if want_P else None)
+
+
+def dora_forward_noalloc(x, W, A, B, m, s, n_in=None, want_P=True, y=None, n_out=None,
+                         P_out=None, U_out=None):
+    """dora_forward on the library's fixed scratch (no workspace argument;
+    the library allocates nothing).  Outputs as dora_forward."""
+    dev = _dev(x)
+    T, d_in = x.shape
+    d_out = W.shape[0]
+    r = A.shape[0]
+    y = torch.empty(T, d_out, dtype=x.dtype, device=dev) if y is None else y
+    n_out = torch.empty(d_out, dtype=torch.float32, device=dev) if n_out is None else n_out
+    if want_P and P_out is None:
+        P_out = torch.empty(T, r, dtype=x.dtype, device=dev)
+    _check(lib().dora_forward_noalloc(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(m), float(s), T,
+                                      d_in, d_out, r, _dt(x), _ptr(y), _ptr(n_out),
+                                      _ptr(P_out if want_P else None), _ptr(n_in), _ptr(U_out),
+                                      _stream(dev)))
     return y, n_out, (P_out if want_P else None)
 
 

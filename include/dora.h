@@ -300,6 +300,30 @@ size_t dora_linear_workspace(int64_t T, int64_t d_in, int64_t d_out, int dtype);
 int dora_linear(const void *x, const void *W, int64_t T, int64_t d_in, int64_t d_out, int dtype,
                 void *y, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * dora_forward_noalloc - dora_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  The arguments and results are those
+ * of dora_forward without ws / ws_bytes; the scratch comes from a fixed
+ * library-owned device array of DORA_NOALLOC_SCRATCH_BYTES (96 MiB), which
+ * every GPU the library runs on holds from the library's load until the
+ * process ends (its address on a device is looked up on the first call
+ * there).  The call allocates nothing.
+ *   Modules whose dora_forward_workspace() exceeds the array are rejected
+ *   with DORA_E_WORKSPACE before anything touches the device.  The forward
+ *   of every module of up to 16384 tokens at widths of the order of 28672
+ *   with r = 384 fits.
+ *   The array is shared by every call on one GPU and keeps the last call's
+ *   contents (nothing in it needs to start at zero): calls that overlap in
+ *   time on one GPU (on different streams or threads) race on it and must
+ *   be serialised by the caller.  The stream's device is the GPU used.
+ */
+#define DORA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int dora_forward_noalloc(const void *x, const void *W, const void *A, const void *B,
+                         const float *m, float s, int64_t T, int64_t d_in, int64_t d_out,
+                         int64_t r, int dtype, void *y, float *n_out, void *P_out,
+                         const float *n_in, float *U_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
