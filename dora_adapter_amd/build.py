@@ -1,4 +1,5 @@
-"""Compile libdora.so (HIP, gfx950) in-tree: dora_adapter_amd/libdora.so.
+"""Compile libdora.so (HIP, gfx950) in-tree: dora_adapter_amd/libdora.so, and
+the benchmark's stream-ceiling helper libstreamceil.so.
 
 Every source is compiled with hipcc for gfx950 only.  Packed-fp32 VALU ops are
 disabled for device code (they are left to scalar fp32 instructions).
@@ -20,7 +21,11 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = [("gemm_bf16.hip", (), "gemm_bf16"), ("gemm_f32.hip", (), "gemm_f32"),
            ("elementwise.hip", (), "elementwise"), ("dora_api.cpp", (), "dora_api"),
            ("noalloc.hip", (), "noalloc")] + \
-          [("gemm_dma_cfg.hip", (f"-DDORA_DMA_CFG={k}",), f"gemm_dma_cfg{k}") for k in range(7)]
+          [("gemm_dma_cfg.hip", (f"-DDORA_DMA_CFG={k}",), f"gemm_dma_cfg{k}") for k in range(8)]
+# Measurement helper for bench.py (not part of the DoRA library): the HBM
+# rate of a plain two-in / one-out stream.
+STREAM_SOURCE = ("stream_ceiling.hip", (), "stream_ceiling")
+STREAM_LIB = os.path.join(HERE, "libstreamceil.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -42,18 +47,24 @@ def _compile(unit, extra=()):
     return obj, err
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib)
+
+
 def build(verbose=False, extra=()):
+    """Build libdora.so and the benchmark's stream-ceiling helper."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+    units = SOURCES + [STREAM_SOURCE]
+    with cf.ThreadPoolExecutor(max_workers=min(len(units), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(lambda s: _compile(s, extra), units))
     for (obj, err) in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-           *[o for o, _ in results]]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    _link([o for o, _ in results[:len(SOURCES)]], LIB)
+    _link([results[-1][0]], STREAM_LIB)
     return LIB
 
 

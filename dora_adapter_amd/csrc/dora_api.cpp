@@ -348,7 +348,7 @@ FwdPlan plan_forward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtyp
 
 struct BwdPlan {
     GPlan q, dx, dB, dA;
-    int64_t t_chunk;
+    int64_t sweep;  // rows per sweep of the dh/dm pass = its dm partial count
     int nchunks;
     size_t o_dh, o_dmpart, o_Q, o_Qpart, o_dxpart, o_dBpart, o_dApart;
     size_t bytes;
@@ -372,8 +372,8 @@ BwdPlan plan_backward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dty
     b.dA = plan_gemm(bf, GemmShape{r, d_in, {T, 0}, 1, 2,
                                    dma_mn_operand(T, r) && dma_mn_operand(T, d_in)},
                      r * d_in);
-    b.t_chunk = dm_t_chunk(T, d_out);
-    b.nchunks = T > 0 ? static_cast<int>((T + b.t_chunk - 1) / b.t_chunk) : 0;
+    b.sweep = T > 0 ? dm_sweep_rows(T, d_out) : 0;
+    b.nchunks = static_cast<int>(b.sweep);
     const size_t e = esize(dtype);
     b.o_dh = cv.take(static_cast<size_t>(T) * d_out * e);
     b.o_dmpart = cv.take(static_cast<size_t>(std::max(b.nchunks, 1)) * d_out * 4);
@@ -1353,7 +1353,7 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
     void *Q = w + p.o_Q;
 
     // 1. dh = g dy and dm partial sums (one pass over dy and y), then dm.
-    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, p.t_chunk, dh, dmpart, st), "dh/dm");
+    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, p.sweep, dh, dmpart, st), "dh/dm");
     DORA_LAUNCH(launch_dm_finish(dmpart, p.nchunks, m, d_out, dm, st), "dm finish");
     // 2. Q = s dh B  (A K-major, B MN-major).
     DORA_CHECK(run_store(bf, p.q, seg1(T, r, dh, d_out, B, r, d_out), 1, Q, r, s,
@@ -1424,7 +1424,7 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
     const size_t gsz = bf ? static_cast<size_t>(r) * r * 2 : 0;  // lo half of a hi/lo pair
 
     // 1-3. As with n held constant: dh = g dy and dm, Q = s dh B, dx = [dh | Q] [W ; A].
-    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, b.t_chunk, dh, dmpart, st), "dh/dm");
+    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, b.sweep, dh, dmpart, st), "dh/dm");
     DORA_LAUNCH(launch_dm_finish(dmpart, b.nchunks, m, d_out, dm, st), "dm finish");
     DORA_CHECK(run_store(bf, b.q, seg1(T, r, dh, d_out, B, r, d_out), 1, Q, r, s,
                          reinterpret_cast<float *>(w + b.o_Qpart), st, "Q = s dh B"));

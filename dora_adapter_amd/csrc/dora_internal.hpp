@@ -136,7 +136,7 @@ hipError_t launch_norm_finish(const float *base_part, int zb, const float *cross
                               const float *gram_part, int zg, int64_t d_out, float s, float *n,
                               float *base, float *cross, float *gram, hipStream_t st);
 hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const float *m,
-                                const float *n, int64_t T, int64_t d_out, int64_t t_chunk,
+                                const float *n, int64_t T, int64_t d_out, int64_t sweep,
                                 void *dh, float *dm_part, hipStream_t st);
 hipError_t launch_dm_finish(const float *dm_part, int nchunks, const float *m, int64_t d_out,
                             float *dm, hipStream_t st);
@@ -181,7 +181,8 @@ hipError_t launch_fill_f32(float *dst, float v, int64_t n, hipStream_t st);
 int set_error(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-// dh/dm partial sums: rows of T per chunk and number of chunks.
-int64_t dm_t_chunk(int64_t T, int64_t d_out);
+// dh/dm pass: rows per sweep of the grid, which is also the number of dm
+// partial sums per column (thread t0 sums rows t0, t0 + sweep, ...).
+int64_t dm_sweep_rows(int64_t T, int64_t d_out);
 
 }  // namespace dora

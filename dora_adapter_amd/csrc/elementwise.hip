@@ -9,10 +9,11 @@
 //   small ones   split-K reduction, Gram matrix finalisation (fp32 sum of
 //                split partials, bf16 hi/lo split) and the row-norm finish.
 //
-// Streaming layout: a thread owns one group of 8 consecutive columns and a
-// contiguous run of rows, so per-column factors (g - 1, g s) are formed once
-// per run and every row access is a 16-byte load/store, consecutive threads
-// covering consecutive 16-byte groups of a row (fully coalesced).
+// Streaming layout: a thread owns one group of 8 consecutive columns and
+// every R-th row from its first, so per-column factors (g - 1, g s) are
+// formed once per thread; every access is a 16-byte load / store and
+// consecutive threads cover consecutive 16-byte groups of a row, the grid
+// sweeping R whole rows at a time (fully coalesced, in address order).
 #include "dora_internal.hpp"
 #include "epilogue.hpp"
 
@@ -20,13 +21,12 @@ namespace dora {
 namespace {
 
 constexpr int EW_THREADS = 256;
-constexpr int UNROLL = 4;  // rows of a streaming run loaded together
-// Threads a streaming launch aims for: 256 CUs x 8 wavefronts x 64 lanes x 4.
-constexpr int64_t EW_TARGET_THREADS = 256LL * 8 * 64 * 4;
-// The compose launch aims for twice that: with two input streams and one
-// output it needs more bytes in flight (measured at 8192 x 28672 bf16: 5.30
-// TB/s at the smaller count, 5.55 at this one, 5.15 at half the smaller one).
-constexpr int64_t COMPOSE_TARGET_THREADS = 2 * EW_TARGET_THREADS;
+// The two-in / one-out streams (compose, dh / dm) run 2^18 threads, about a
+// quarter million 16-byte vectors in flight per sweep: the launch shape at
+// which a plain stream of this pattern moves the most bytes at every
+// workload size measured (4096 x 4096 to 16384 x 27648 bf16: 5.0 - 5.9 TB/s
+// with the MALL flushed, against 4.4 - 5.6 at 2^20 threads).
+constexpr int64_t STREAM_THREADS = int64_t(1) << 18;
 
 // 16-byte streaming accesses with the nontemporal hint: data read or written
 // once per launch should not displace what other waves still reuse (about
@@ -86,16 +86,19 @@ struct Vec8<float> {
     __device__ static void store1(float *p, float v) { *p = v; }
 };
 
-// Rows per thread run for a [T, d_out] stream with gpr column groups.
-__host__ __device__ inline int64_t rows_per_run(int64_t T, int64_t gpr,
-                                                int64_t target = EW_TARGET_THREADS)
+// Rows a [T, d_out] stream with gpr 16-byte column groups advances per
+// sweep: thread g takes column group g % gpr and rows g / gpr, g / gpr + R,
+// g / gpr + 2 R, ..., so that per-column factors are formed once per thread
+// and every sweep of the grid reads R whole consecutive rows (the memory is
+// streamed in address order).
+__host__ __device__ inline int64_t sweep_rows(int64_t T, int64_t gpr)
 {
-    int64_t runs = target / (gpr > 0 ? gpr : 1);
-    if (runs < 1)
-        runs = 1;
-    if (runs > T)
-        runs = T;
-    return runs > 0 ? (T + runs - 1) / runs : 1;
+    int64_t R = (STREAM_THREADS + gpr / 2) / (gpr > 0 ? gpr : 1);
+    if (R < 1)
+        R = 1;
+    if (R > T)
+        R = T;
+    return R;
 }
 
 // One compose element in the stable form: y = b + ((g - 1) b + g s l).
@@ -108,20 +111,18 @@ template <typename T, bool VEC>
 __global__ void __launch_bounds__(EW_THREADS)
     compose_kernel(const T *__restrict__ base, const T *__restrict__ lora,
                    const float *__restrict__ m, const float *__restrict__ n, float s, int64_t Tn,
-                   int64_t d_out, int64_t rows, T *y)
+                   int64_t d_out, int64_t R, T *y)
 {
     const int64_t gpr = (d_out + 7) / 8;
     const int64_t gi = static_cast<int64_t>(blockIdx.x) * EW_THREADS + threadIdx.x;
-    const int64_t c = gi % gpr, run = gi / gpr;
-    const int64_t t0 = run * rows;
-    if (t0 >= Tn)
+    const int64_t c = gi % gpr, t0 = gi / gpr;
+    if (t0 >= R)
         return;
-    const int64_t t1 = (t0 + rows) < Tn ? (t0 + rows) : Tn;
     const int64_t i0 = c * 8;
     const int cnt = (d_out - i0) < 8 ? static_cast<int>(d_out - i0) : 8;
-    // per-column factors, once per run, each rounded once to fp32 from fp64
-    // (g - 1 = (m - n) / n and g s = m s / n): the lora term then carries two
-    // roundings (g s, its product with lora) instead of three
+    // per-column factors, once per thread, each rounded once to fp32 from
+    // fp64 (g - 1 = (m - n) / n and g s = m s / n): the lora term then
+    // carries two roundings (g s, its product with lora) instead of three
     float gm1[8], gs[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -130,30 +131,11 @@ __global__ void __launch_bounds__(EW_THREADS)
         gm1[q] = static_cast<float>((mi - ni) / ni);
         gs[q] = static_cast<float>(mi * static_cast<double>(s) / ni);
     }
-    if (VEC) {
-        // UNROLL rows per iteration, all loads before any store: y may be
-        // base itself (each element is read before it is written, by the
-        // same thread), so the compiler would otherwise keep one row of loads
-        // in flight per thread
-        int64_t t = t0;
-        for (; t + UNROLL <= t1; t += UNROLL) {
-            float b[UNROLL][8], l[UNROLL][8];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                Vec8<T>::load(base + (t + u) * d_out + i0, b[u]);
-                Vec8<T>::load(lora + (t + u) * d_out + i0, l[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                float o[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    o[q] = compose1(b[u][q], l[u][q], gm1[q], gs[q]);
-                Vec8<T>::store(y + (t + u) * d_out + i0, o);
-            }
-        }
-        for (; t < t1; ++t) {
-            const int64_t off = t * d_out + i0;
+    // y may be base itself: each element is read, then written, by the same
+    // thread
+    for (int64_t t = t0; t < Tn; t += R) {
+        const int64_t off = t * d_out + i0;
+        if (VEC) {
             float b[8], l[8], o[8];
             Vec8<T>::load(base + off, b);
             Vec8<T>::load(lora + off, l);
@@ -161,10 +143,7 @@ __global__ void __launch_bounds__(EW_THREADS)
             for (int q = 0; q < 8; ++q)
                 o[q] = compose1(b[q], l[q], gm1[q], gs[q]);
             Vec8<T>::store(y + off, o);
-        }
-    } else {
-        for (int64_t t = t0; t < t1; ++t) {
-            const int64_t off = t * d_out + i0;
+        } else {
             for (int q = 0; q < cnt; ++q)
                 Vec8<T>::store1(y + off + q, compose1(Vec8<T>::load1(base + off + q),
                                                       Vec8<T>::load1(lora + off + q), gm1[q],
@@ -173,19 +152,19 @@ __global__ void __launch_bounds__(EW_THREADS)
     }
 }
 
+// dh = g dy and dm partial sums: thread (column group c, first row t0)
+// sums dy y over rows t0, t0 + R, ... into dm_part[t0][c * 8 ..].
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(EW_THREADS)
     dh_dm_kernel(const T *__restrict__ dy, const T *__restrict__ yv, const float *__restrict__ m,
-                 const float *__restrict__ n, int64_t Tn, int64_t d_out, int64_t rows,
+                 const float *__restrict__ n, int64_t Tn, int64_t d_out, int64_t R,
                  T *__restrict__ dh, float *__restrict__ dm_part)
 {
     const int64_t gpr = (d_out + 7) / 8;
     const int64_t gi = static_cast<int64_t>(blockIdx.x) * EW_THREADS + threadIdx.x;
-    const int64_t c = gi % gpr, run = gi / gpr;
-    const int64_t t0 = run * rows;
-    if (t0 >= Tn)
+    const int64_t c = gi % gpr, t0 = gi / gpr;
+    if (t0 >= R)
         return;
-    const int64_t t1 = (t0 + rows) < Tn ? (t0 + rows) : Tn;
     const int64_t i0 = c * 8;
     const int cnt = (d_out - i0) < 8 ? static_cast<int>(d_out - i0) : 8;
     float g[8], acc[8];
@@ -194,28 +173,9 @@ __global__ void __launch_bounds__(EW_THREADS)
         g[q] = q < cnt ? m[i0 + q] / n[i0 + q] : 0.f;
         acc[q] = 0.f;
     }
-    if (VEC) {
-        int64_t t = t0;
-        for (; t + UNROLL <= t1; t += UNROLL) {
-            float a[UNROLL][8], b[UNROLL][8];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                Vec8<T>::load(dy + (t + u) * d_out + i0, a[u]);
-                Vec8<T>::load(yv + (t + u) * d_out + i0, b[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                float o[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    o[q] = g[q] * a[u][q];
-                    acc[q] = __fmaf_rn(a[u][q], b[u][q], acc[q]);
-                }
-                Vec8<T>::store(dh + (t + u) * d_out + i0, o);
-            }
-        }
-        for (; t < t1; ++t) {
-            const int64_t off = t * d_out + i0;
+    for (int64_t t = t0; t < Tn; t += R) {
+        const int64_t off = t * d_out + i0;
+        if (VEC) {
             float a[8], b[8], o[8];
             Vec8<T>::load(dy + off, a);
             Vec8<T>::load(yv + off, b);
@@ -225,10 +185,7 @@ __global__ void __launch_bounds__(EW_THREADS)
                 acc[q] = __fmaf_rn(a[q], b[q], acc[q]);
             }
             Vec8<T>::store(dh + off, o);
-        }
-    } else {
-        for (int64_t t = t0; t < t1; ++t) {
-            const int64_t off = t * d_out + i0;
+        } else {
             for (int q = 0; q < cnt; ++q) {
                 const float a = Vec8<T>::load1(dy + off + q);
                 Vec8<T>::store1(dh + off + q, g[q] * a);
@@ -237,7 +194,7 @@ __global__ void __launch_bounds__(EW_THREADS)
         }
     }
     for (int q = 0; q < cnt; ++q)
-        dm_part[run * d_out + i0 + q] = acc[q];
+        dm_part[t0 * d_out + i0 + q] = acc[q];
 }
 
 __global__ void dm_finish_kernel(const float *__restrict__ part, int nchunks,
@@ -481,9 +438,9 @@ unsigned blocks_for(int64_t threads)
 
 }  // namespace
 
-int64_t dm_t_chunk(int64_t T, int64_t d_out)
+int64_t dm_sweep_rows(int64_t T, int64_t d_out)
 {
-    return rows_per_run(T, (d_out + 7) / 8);
+    return sweep_rows(T, (d_out + 7) / 8);
 }
 
 hipError_t launch_compose(int bf16, const void *base, const void *lora, const float *m,
@@ -493,9 +450,8 @@ hipError_t launch_compose(int bf16, const void *base, const void *lora, const fl
     if (T == 0 || d_out == 0)
         return hipSuccess;
     const int64_t gpr = (d_out + 7) / 8;
-    const int64_t rows = rows_per_run(T, gpr, COMPOSE_TARGET_THREADS);
-    const int64_t runs = (T + rows - 1) / rows;
-    const dim3 grid(blocks_for(gpr * runs));
+    const int64_t R = sweep_rows(T, gpr);
+    const dim3 grid(blocks_for(gpr * R));
     const bool vec = (d_out % 8) == 0;
     if (bf16) {
         auto *b = static_cast<const uint16_t *>(base);
@@ -503,33 +459,32 @@ hipError_t launch_compose(int bf16, const void *base, const void *lora, const fl
         auto *o = static_cast<uint16_t *>(y);
         if (vec)
             hipLaunchKernelGGL((compose_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0, st, b, l,
-                               m, n, s, T, d_out, rows, o);
+                               m, n, s, T, d_out, R, o);
         else
             hipLaunchKernelGGL((compose_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0, st, b,
-                               l, m, n, s, T, d_out, rows, o);
+                               l, m, n, s, T, d_out, R, o);
     } else {
         auto *b = static_cast<const float *>(base);
         auto *l = static_cast<const float *>(lora);
         auto *o = static_cast<float *>(y);
         if (vec)
             hipLaunchKernelGGL((compose_kernel<float, true>), grid, dim3(EW_THREADS), 0, st, b, l, m,
-                               n, s, T, d_out, rows, o);
+                               n, s, T, d_out, R, o);
         else
             hipLaunchKernelGGL((compose_kernel<float, false>), grid, dim3(EW_THREADS), 0, st, b, l,
-                               m, n, s, T, d_out, rows, o);
+                               m, n, s, T, d_out, R, o);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const float *m,
-                                const float *n, int64_t T, int64_t d_out, int64_t t_chunk,
+                                const float *n, int64_t T, int64_t d_out, int64_t R,
                                 void *dh, float *dm_part, hipStream_t st)
 {
     if (T == 0 || d_out == 0)
         return hipSuccess;
     const int64_t gpr = (d_out + 7) / 8;
-    const int64_t runs = (T + t_chunk - 1) / t_chunk;
-    const dim3 grid(blocks_for(gpr * runs));
+    const dim3 grid(blocks_for(gpr * R));
     const bool vec = (d_out % 8) == 0;
     if (bf16) {
         auto *a = static_cast<const uint16_t *>(dy);
@@ -537,20 +492,20 @@ hipError_t launch_dh_dm_partial(int bf16, const void *dy, const void *y, const f
         auto *o = static_cast<uint16_t *>(dh);
         if (vec)
             hipLaunchKernelGGL((dh_dm_kernel<uint16_t, true>), grid, dim3(EW_THREADS), 0, st, a, b,
-                               m, n, T, d_out, t_chunk, o, dm_part);
+                               m, n, T, d_out, R, o, dm_part);
         else
             hipLaunchKernelGGL((dh_dm_kernel<uint16_t, false>), grid, dim3(EW_THREADS), 0, st, a, b,
-                               m, n, T, d_out, t_chunk, o, dm_part);
+                               m, n, T, d_out, R, o, dm_part);
     } else {
         auto *a = static_cast<const float *>(dy);
         auto *b = static_cast<const float *>(y);
         auto *o = static_cast<float *>(dh);
         if (vec)
             hipLaunchKernelGGL((dh_dm_kernel<float, true>), grid, dim3(EW_THREADS), 0, st, a, b, m,
-                               n, T, d_out, t_chunk, o, dm_part);
+                               n, T, d_out, R, o, dm_part);
         else
             hipLaunchKernelGGL((dh_dm_kernel<float, false>), grid, dim3(EW_THREADS), 0, st, a, b, m,
-                               n, T, d_out, t_chunk, o, dm_part);
+                               n, T, d_out, R, o, dm_part);
     }
     return hipGetLastError();
 }

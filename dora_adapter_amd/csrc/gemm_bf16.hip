@@ -365,6 +365,11 @@ constexpr TileCfg kCfgs[] = {
     {128, 384, GEMM_DMA_BK, true, 0.77f, true, true, true, false},
     // 4 waves (4 x 1): the same with M = r (Q^T x)
     {384, 128, GEMM_DMA_BK, true, 0.77f, true, false, false, false},
+    // 8 waves (2 x 4, 64 x 96 per wave): the rank-384 row block with two
+    // waves per SIMD, which hide each other's waits (measured on the
+    // norm's row-dot products against the 4-wave tile: W A^T 231 -> 208 us,
+    // B G 42 -> 28 us at d_out 28672, d_in 8192, r 384)
+    {128, 384, GEMM_DMA_BK, true, 0.85f, true, true, true, false},
 };
 
 }  // namespace
@@ -460,6 +465,8 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
         return launch_dma_128x384(a, layout, rowsq, st);
     case 8:
         return launch_dma_384x128(a, layout, rowsq, st);
+    case 9:
+        return launch_dma_128x384w8(a, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -484,6 +491,8 @@ hipError_t launch_gemm_bf16_grouped(GemmGroup &g, int layout, int cfg, bool rows
         return launch_dma_group_128x384(g, layout, rowsq, st);
     case 8:
         return launch_dma_group_384x128(g, layout, rowsq, st);
+    case 9:
+        return launch_dma_group_128x384w8(g, layout, rowsq, st);
     default:
         return hipErrorInvalidValue;
     }

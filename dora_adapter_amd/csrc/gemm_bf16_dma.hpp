@@ -164,8 +164,15 @@ __device__ __forceinline__ int range_bytes(int64_t bytes)
 // Per-lane offsets are pre-reduced by the instruction offset and raised by
 // GROUP_BIAS, and the descriptor base is lowered by GROUP_BIAS, which keeps
 // every offset non-negative.
+// A tile whose loads per wave are not a multiple of four groups them in
+// twos (or ones); the bias stays that of a group of four.
 constexpr int GROUP = 4;
 constexpr uint32_t GROUP_BIAS = (GROUP - 1) * 1024;
+template <int PA, int PB>
+constexpr int group_size()
+{
+    return (PA % 4 == 0 && PB % 4 == 0) ? 4 : (PA % 2 == 0 && PB % 2 == 0) ? 2 : 1;
+}
 
 // Buffer descriptor over one operand matrix (raw, byte-addressed; dword 3 =
 // 0x00020000 selects plain linear addressing on gfx9-family parts), with its
@@ -225,12 +232,12 @@ constexpr int LOAD_ANY = 0, LOAD_SEG0 = 1, LOAD_SEG1 = 2, LOAD_NONE = 3;
 //   tile; lane l fetches the chunk that belongs at byte 16 l.  A stage adds
 //   k0 * ld * 2 to the per-lane offset (rows past K are out of range and
 //   load as zeros).
-template <bool KMAJ, int R, int NW>
+template <bool KMAJ, int R, int NW, int G = GROUP>
 struct OperandDma {
     static constexpr int NINST = R * ROW_BYTES / 1024;
     static_assert(NINST % NW == 0, "tile loads must split over wavefronts");
     static constexpr int PER = NINST / NW;
-    static_assert(PER % GROUP == 0, "whole load groups per wave");
+    static_assert(PER % G == 0 && G <= GROUP, "whole load groups per wave");
     static constexpr int PITCH = R * 2;  // MN-major row bytes
     static_assert(KMAJ || R >= 128, "MN-major tiles need >= 16 chunks per row");
     uint32_t off[PER];
@@ -242,7 +249,7 @@ struct OperandDma {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int blk = wave * PER + i;
-            const uint32_t bias = GROUP_BIAS - (i % GROUP) * 1024;
+            const uint32_t bias = GROUP_BIAS - (i % G) * 1024;
             if constexpr (KMAJ) {
                 const int rloc = blk * 8 + (lane >> 3);
                 const int chunk = (lane & 7) ^ swz(rloc);
@@ -327,13 +334,15 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                                               const int z)
 {
     using C = DmaCfg<BM, BN, WM, WN>;
-    using DA = OperandDma<AK, BM, WM * WN>;
-    using DB = OperandDma<BKM, BN, WM * WN>;
+    constexpr int G = group_size<(BM * ROW_BYTES / 1024) / (WM * WN),
+                                 (BN * ROW_BYTES / 1024) / (WM * WN)>();
+    using DA = OperandDma<AK, BM, WM * WN, G>;
+    using DB = OperandDma<BKM, BN, WM * WN, G>;
     constexpr int NT = C::NT;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold 32x32 MFMA tiles");
-    static_assert(!ROWSQ || (AK && WM == 1), "row sums of squares: K-major A, all rows in every wave");
+    static_assert(!ROWSQ || AK, "row sums of squares: K-major A");
     static_assert(DA::PER + DB::PER == C::LPS, "load count");
 
     __shared__ __align__(1024) unsigned char smem[C::SMEM];
@@ -382,7 +391,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     // of this split go through descriptors with an empty range: they fetch
     // nothing and deposit zeros in a slot no later stage reads, so every
     // stage has the same shape (no branches, the same vmcnt bookkeeping).
-    constexpr int GA = DA::PER / GROUP, NG = C::LPS / GROUP;
+    constexpr int GA = DA::PER / G, NG = C::LPS / G;
     //
     // MODE (compile-time at each call site) removes the per-lane selects
     // from the common stages: LOAD_SEG0 / LOAD_SEG1 for live stages lying
@@ -394,7 +403,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     struct Group {
         __amdgpu_buffer_rsrc_t rs;
         uint32_t soff;
-        uint32_t v[GROUP];
+        uint32_t v[G];
     };
     auto dma_prep = [&](int64_t sd, int d, auto mode_c) {
         constexpr int MODE = decltype(mode_c)::value;
@@ -405,9 +414,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         // groups of the operand whose loads take longer go first and get the
         // most time to land: A (x, dh rows) for a K-major B, B (a weight
         // read MN-major) otherwise (measured both ways on x W^T and dh W)
-        constexpr int GB = DB::PER / GROUP;
+        constexpr int GB = DB::PER / G;
         const bool isa = BKM ? d < GA : d >= GB;
-        const int i0 = (isa ? (BKM ? d : d - GB) : (BKM ? d - GA : d)) * GROUP;
+        const int i0 = (isa ? (BKM ? d : d - GB) : (BKM ? d - GA : d)) * G;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
             reinterpret_cast<uintptr_t>((lds_void *)(slot(sd) + (isa ? 0 : C::A_BYTES) +
                                                      (wave * (isa ? DA::PER : DB::PER) + i0) *
@@ -420,7 +429,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             rs = scalar_rsrc(sg1 ? g.seg[1].a : g.seg[0].a, live ? (sg1 ? na1 : na0) : 0);
             const int64_t ld = sg1 ? g.seg[1].lda : g.seg[0].lda;
 #pragma unroll
-            for (int j = 0; j < GROUP; ++j) {
+            for (int j = 0; j < G; ++j) {
                 const uint32_t off = sg1 ? da1.off[i0 + j] : da0.off[i0 + j];
                 if constexpr (AK) {
                     const uint32_t kq = sg1 ? da1.kch[i0 + j] : da0.kch[i0 + j];
@@ -434,7 +443,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             rs = scalar_rsrc(sg1 ? g.seg[1].b : g.seg[0].b, live ? (sg1 ? nb1 : nb0) : 0);
             const int64_t ld = sg1 ? g.seg[1].ldb : g.seg[0].ldb;
 #pragma unroll
-            for (int j = 0; j < GROUP; ++j) {
+            for (int j = 0; j < G; ++j) {
                 const uint32_t off = sg1 ? db1.off[i0 + j] : db0.off[i0 + j];
                 if constexpr (BKM) {
                     const uint32_t kq = sg1 ? db1.kch[i0 + j] : db0.kch[i0 + j];
@@ -464,11 +473,12 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.f;
     // ROWSQ: sums of squares of A's rows from the A fragments already in
-    // registers (every wave holds all BM rows): lane l covers row
-    // i * 32 + (l & 31) of block i and K half l >> 5 of each 16-wide step.
-    // Every wave sums every block (branch-free, two v_dot2_f32_bf16 chains
-    // per block, spread over the first MFMAs of a half) and keeps blocks
-    // i = wn, wn + WN, ... at the end.
+    // registers (every wave of a wave row holds all of that row's WTM tile
+    // rows): lane l covers row wm * WTM + i * 32 + (l & 31) of block i and K
+    // half l >> 5 of each 16-wide step.  Every wave sums every block of its
+    // rows (branch-free, two v_dot2_f32_bf16 chains per block, spread over
+    // the first MFMAs of a half) and keeps blocks i = wn, wn + WN, ... at the
+    // end.
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     float sq[ROWSQ ? TM : 1][2];
 #pragma unroll
@@ -501,7 +511,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     auto half = [&](auto h_c, int64_t D, FR &cur, FR &nxt, auto mode_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr bool MODE_LOADS = decltype(mode_c)::value != LOAD_NONE;
-        constexpr int NLH = H == 1 && MODE_LOADS ? NG * GROUP : 0;  // loads in this half
+        constexpr int NLH = H == 1 && MODE_LOADS ? NG * G : 0;  // loads in this half
         constexpr int NOPS = NRD + NLH;
         // the reads of `cur` were issued during the previous half: retire
         // them here, so that no wait lands inside the interleaved sequence
@@ -533,13 +543,13 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 constexpr int o = q * NOPS / SPAN + decltype(oc)::value;
                 // loads spread evenly, from the first slot on (they have a
                 // deadline; the reads only feed the next half); load li is
-                // number li % GROUP of group li / GROUP
+                // number li % G of group li / G
                 constexpr int li = NLH > 0 && (o * NLH) % NOPS < NLH ? (o * NLH) / NOPS : -1;
                 constexpr int rd = o - (o * NLH + NOPS - 1) / NOPS;
                 if constexpr (li >= 0) {
-                    if constexpr (li % GROUP == 0)
-                        grp = dma_prep(D + 2, li / GROUP, mode_c);
-                    issue(grp, std::integral_constant<int, li % GROUP>{});
+                    if constexpr (li % G == 0)
+                        grp = dma_prep(D + 2, li / G, mode_c);
+                    issue(grp, std::integral_constant<int, li % G>{});
                 } else {
                     read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, rd>(nxt, An, Bn, 1 - H, wm, wn,
                                                                     lane);
@@ -558,7 +568,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
 #pragma unroll
             for (int d = 0; d < NG; ++d) {
                 const Group grp = dma_prep(s_begin + p, d, std::integral_constant<int, LOAD_ANY>{});
-                static_for<GROUP>([&](auto jc) { issue(grp, jc); });
+                static_for<G>([&](auto jc) { issue(grp, jc); });
             }
         wait_vmcnt<C::LPS>();  // stage s_begin has landed
         stage_barrier();
@@ -606,7 +616,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                     if (b == i)
                         su = sq[b][0] + sq[b][1];
                 const float t = su + __shfl_xor(su, 32);
-                const int64_t row = m0 + i * 32 + lane;
+                const int64_t row = m0 + wm * WTM + i * 32 + lane;
                 if (i < TM && lane < 32 && row < g.M)
                     g.rowsq[static_cast<int64_t>(z) * g.M + row] = t;
             }

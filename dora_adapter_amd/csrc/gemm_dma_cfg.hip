@@ -74,6 +74,26 @@ template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 1, 4, true,
     GemmGroup);
 template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 1, 4, true, false, false>(
     GemmGroup);
+#elif DORA_DMA_CFG == 7
+// 128 x 384 with eight waves (2 x 4), with and without the row sums of squares
+template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 2, 4, true, true, true>(GemmArgs);
+template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 2, 4, true, true, false>(GemmArgs);
+template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 2, 4, true, false, false>(GemmArgs);
+template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 2, 4, false, false, false>(GemmArgs);
+template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 2, 4, true, true, true>(
+    GemmGroup);
+template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 2, 4, true, true, false>(
+    GemmGroup);
+template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 384, 2, 4, true, false, false>(
+    GemmGroup);
+hipError_t launch_dma_128x384w8(const GemmArgs &a, int layout, bool rowsq, hipStream_t st)
+{
+    return dma::launch_dma_layout<128, 384, 2, 4>(a, layout, rowsq, st);
+}
+hipError_t launch_dma_group_128x384w8(GemmGroup &g, int layout, bool rowsq, hipStream_t st)
+{
+    return dma::launch_dma_group_layout<128, 384, 2, 4>(g, layout, rowsq, st);
+}
 #else
 #error "DORA_DMA_CFG out of range"
 #endif

@@ -27,7 +27,7 @@ hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStrea
     switch (layout) {
     case 0:
         if (rowsq) {
-            if constexpr (WM == 1)
+            if constexpr (BM == 128 && BN == 384)
                 return launch_dma<BM, BN, WM, WN, true, true, true>(a, st);
             else
                 return hipErrorInvalidValue;
@@ -67,7 +67,7 @@ hipError_t launch_dma_group_layout(GemmGroup &g, int layout, bool rowsq, hipStre
     switch (layout) {
     case 0:
         if (rowsq) {
-            if constexpr (WM == 1)
+            if constexpr (BM == 128 && BN == 384)
                 return launch_dma_group<BM, BN, WM, WN, true, true, true>(g, st);
             else
                 return hipErrorInvalidValue;
@@ -95,6 +95,7 @@ DORA_DMA_LAUNCHERS(256, 128)
 DORA_DMA_LAUNCHERS(128, 128)
 DORA_DMA_LAUNCHERS(128, 384)
 DORA_DMA_LAUNCHERS(384, 128)
+DORA_DMA_LAUNCHERS(128, 384w8)
 #undef DORA_DMA_LAUNCHERS
 
 }  // namespace dora

@@ -27,16 +27,30 @@ def test_peaks():
 
 
 def test_norm_flops_terms():
+    """The algorithmic count: B G once (the kernels' split of G into a bf16
+    hi/lo pair is an implementation choice, not work the method asks for)."""
     d_out, d_in, r = 28672, 8192, 384
     u = 2 * d_out * d_in * r          # U = W A^T
     g = 2 * r * r * d_in              # G = A A^T
-    bg = 2 * (2 * d_out * r * r)      # B G_hi and B G_lo
+    bg = 2 * d_out * r * r            # B G
     base = 2 * d_out * d_in           # row sums of W^2
     dots = 2 * (2 * d_out * r)        # cross and Gram row dots
     assert bench.norm_flops(d_out, d_in, r) == u + g + bg + base + dots
     # the square and MLP shapes scale the same way
-    assert bench.norm_flops(64, 128, 8) == (2 * 64 * 128 * 8 + 2 * 8 * 8 * 128 + 4 * 64 * 8 * 8
+    assert bench.norm_flops(64, 128, 8) == (2 * 64 * 128 * 8 + 2 * 8 * 8 * 128 + 2 * 64 * 8 * 8
                                             + 2 * 64 * 128 + 4 * 64 * 8)
+
+
+def test_config_choices_and_workloads():
+    assert bench.parse_args([]).config == "c5"
+    for c in bench.CONFIGS:
+        assert bench.parse_args(["--config", c]).config == c
+        shapes = bench.workload(c)
+        assert all(sh.dtype == "bf16" for sh in shapes)
+    up, down = bench.workload("c4")
+    assert (up.d_in, up.d_out, down.d_in, down.d_out) == (5120, 27648, 27648, 5120)
+    assert up.T == down.T == 16384 and up.r == down.r == 384
+    assert bench.workload("c5")[0].backward
 
 
 def test_traffic_record_describes_the_base_product():

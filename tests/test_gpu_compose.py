@@ -2,12 +2,12 @@
 y = (m/n)(base + s*lora), including the near-unity regime where g = m/n is
 within 1e-6 .. 1e-2 of one.
 
-A thread of the compose kernel streams one 8-column group down a run of
-consecutive rows, four rows at a time with a row-by-row tail; the run length
-grows with T * d_out.  The large cases below give runs of 5, 9 and 29 rows
-(the last at the benchmarked 8192 x 28672 output, with a shorter last run),
-so both the four-row blocks and the tail are compared, in place and out of
-place."""
+A thread of the compose kernel streams one 8-column group down every R-th
+row from its first (the grid sweeps R whole rows at a time, R about 2^18
+threads over the column groups).  The large cases below make R not divide T,
+so the last sweep is partial and threads take different row counts (at the
+benchmarked 8192 x 28672 output R = 73: 112 or 113 rows per thread), in
+place and out of place."""
 import numpy as np
 import pytest
 import torch
@@ -111,21 +111,20 @@ def test_compose_deterministic():
     assert torch.equal(a, b)
 
 
-def _run_length(T, d_out, target=2 * 256 * 8 * 64 * 4):
-    """Rows per thread run of the compose launch (it aims for 2^20 threads)."""
+def _sweep_rows(T, d_out, threads=1 << 18):
+    """Rows per sweep of the compose launch (2^18 threads over the column groups)."""
     gpr = (d_out + 7) // 8
-    runs = max(min(target // gpr, T), 1)
-    return -(-T // runs)
+    return max(min((threads + gpr // 2) // gpr, T), 1)
 
 
 @pytest.mark.parametrize("T,d_out,dtype,rows", [
-    (4100, 8192, torch.bfloat16, 5),      # one four-row block and a one-row tail
-    (4100, 16384, torch.float32, 9),      # two blocks and a tail, fp32
+    (4100, 8192, torch.bfloat16, 256),    # 16 whole sweeps and 4 rows
+    (4100, 16384, torch.float32, 128),    # 32 whole sweeps and 4 rows, fp32
 ])
 @pytest.mark.parametrize("in_place", [False, True])
-def test_compose_unrolled_runs_full(T, d_out, dtype, rows, in_place):
-    assert _run_length(T, d_out) == rows
-    say("compose unrolled runs", T, d_out, dtype, "in place" if in_place else "out of place")
+def test_compose_sweeps_full(T, d_out, dtype, rows, in_place):
+    assert _sweep_rows(T, d_out) == rows and T % rows
+    say("compose sweeps", T, d_out, dtype, "in place" if in_place else "out of place")
     base, lora, m, n = _inputs(T, d_out, dtype, seed=T + d_out + in_place)
     s = 0.75
     gb = gpu(base)
@@ -138,12 +137,11 @@ def test_compose_unrolled_runs_full(T, d_out, dtype, rows, in_place):
 @pytest.mark.parametrize("T", [8192, 8191])
 @pytest.mark.parametrize("in_place", [False, True])
 def test_compose_benchmark_shape_rows(T, in_place):
-    """The benchmarked output, 8192 x 28672 bf16 (runs of 29 rows: seven
-    four-row blocks and a tail; the last run shorter), and 8191 rows.  Every
-    column of the first 64 rows, the last 64 rows and 64 sampled rows is
-    compared with the oracle."""
+    """The benchmarked output, 8192 x 28672 bf16 (sweeps of 73 rows, the last
+    one partial), and 8191 rows.  Every column of the first 64 rows, the last
+    64 rows and 64 sampled rows is compared with the oracle."""
     d_out, dtype = 28672, torch.bfloat16
-    assert _run_length(T, d_out) == 29
+    assert _sweep_rows(T, d_out) == 73 and T % 73
     say("compose benchmark shape", T, d_out, "in place" if in_place else "out of place")
     base, lora, m, n = _inputs(T, d_out, dtype, seed=T + in_place)
     s = 1.0

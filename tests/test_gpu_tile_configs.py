@@ -22,7 +22,7 @@ from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
 
-N_CFGS = 9  # register-staged 0-3, direct-to-LDS 4-8
+N_CFGS = 10  # register-staged 0-3, direct-to-LDS 4-9
 
 SHAPES = [
     # T, d_out, d_in, r, s
