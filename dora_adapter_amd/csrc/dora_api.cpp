@@ -144,18 +144,19 @@ int forced_tile_cfg()
 // split, writing and re-reading `part_per_split` fp32 values per split and
 // one extra launch.  A split keeps at least 512 K values and its partials
 // under 1 GiB.
-GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split)
+GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split, int only = -1)
 {
     const double cu_flops = bf16 ? 4.0e12 : 157.3e12 / kCUs * 0.5;
     const double hbm = 5.0e12;
     GPlan best;
     double best_cost = -1.0;
     const int ncfg = bf16 ? gemm_bf16_num_cfgs() : 1;
-    const int forced = bf16 ? forced_tile_cfg() : -1;
+    // `only`: plan that configuration alone (a product only it implements)
+    const int forced = bf16 ? (only >= 0 ? only : forced_tile_cfg()) : -1;
     const bool ragged = bf16 && shape_ragged(sh);
     // pass 0: the forced configuration only (if any); pass 1: all of them,
     // when pass 0 found none that serves this product
-    for (int pass = forced >= 0 ? 0 : 1; pass < 2 && best_cost < 0; ++pass)
+    for (int pass = forced >= 0 ? 0 : 1; pass < (only >= 0 ? 1 : 2) && best_cost < 0; ++pass)
     for (int c = 0; c < ncfg; ++c) {
         int BM, BN, bk;
         float rel;
@@ -348,8 +349,11 @@ FwdPlan plan_forward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dtyp
 
 struct BwdPlan {
     GPlan q, dx, dB, dA;
-    int64_t sweep;  // rows per sweep of the dh/dm pass = its dm partial count
-    int nchunks;
+    // dh and the dm sums formed inside the dB product (one pass over dy and
+    // y that also computes dB), else by the separate dh/dm pass
+    bool fused_dhdm;
+    int64_t sweep;  // rows per sweep of the dh/dm pass
+    int nchunks;    // dm partial sums per column
     size_t o_dh, o_dmpart, o_Q, o_Qpart, o_dxpart, o_dBpart, o_dApart;
     size_t bytes;
 };
@@ -366,14 +370,26 @@ BwdPlan plan_backward(int64_t T, int64_t d_in, int64_t d_out, int64_t r, int dty
                                    dma_operand(T, d_out) && dma_mn_operand(d_out, d_in) &&
                                        dma_operand(T, r) && dma_mn_operand(r, d_in)},
                      T * d_in);
-    b.dB = plan_gemm(bf, GemmShape{d_out, r, {T, 0}, 1, 2,
-                                   dma_mn_operand(T, d_out) && dma_mn_operand(T, r)},
-                     d_out * r);
+    const GemmShape dbs{d_out, r, {T, 0}, 1, 2, dma_mn_operand(T, d_out) && dma_mn_operand(T, r)};
     b.dA = plan_gemm(bf, GemmShape{r, d_in, {T, 0}, 1, 2,
                                    dma_mn_operand(T, r) && dma_mn_operand(T, d_in)},
                      r * d_in);
+    // dh/dm inside the dB product: bf16, the pipelined layout, tokens to
+    // stream, and no tile configuration other than the one that implements
+    // it requested (a test restricting the planners to another one runs the
+    // separate pass)
+    const int forced = forced_tile_cfg();
+    b.fused_dhdm = false;
+    if (bf && dbs.dma_ok && T > 0)
+        for (int c = 0; c < gemm_bf16_num_cfgs() && !b.fused_dhdm; ++c)
+            if (gemm_bf16_cfg(c).dhdm_ok && (forced < 0 || forced == c)) {
+                b.dB = plan_gemm(bf, dbs, d_out * r, c);
+                b.fused_dhdm = b.dB.cfg == c;
+            }
+    if (!b.fused_dhdm)
+        b.dB = plan_gemm(bf, dbs, d_out * r);
     b.sweep = T > 0 ? dm_sweep_rows(T, d_out) : 0;
-    b.nchunks = static_cast<int>(b.sweep);
+    b.nchunks = b.fused_dhdm ? b.dB.splits : static_cast<int>(b.sweep);
     const size_t e = esize(dtype);
     b.o_dh = cv.take(static_cast<size_t>(T) * d_out * e);
     b.o_dmpart = cv.take(static_cast<size_t>(std::max(b.nchunks, 1)) * d_out * 4);
@@ -585,6 +601,33 @@ int run_store(bool bf16, const GPlan &p, GemmArgs a, int layout, void *out, int6
         DORA_LAUNCH(run_gemm(bf16, p, a, layout, false, st), what);
         DORA_LAUNCH(launch_splitk_reduce(bf16, part, p.splits, a.M, a.N, alpha, out, st), what);
     }
+    return DORA_OK;
+}
+
+// dh = g dy, the dm partial sums and the dB product in one pass over dy and
+// y (BwdPlan::fused_dhdm): alpha dh^T P stored to `out` in the element type
+// when `f32` is 0 (unsplit plans only), else as fp32 split slots (slot z at
+// out + z d_out r).
+int run_dhdm_dB(const BwdPlan &b, const void *dy, const void *y, const float *m, const float *n,
+                const void *P, int64_t T, int64_t d_out, int64_t r, void *dh, float *dmpart,
+                void *out, int f32, float alpha, hipStream_t st)
+{
+    if (!f32 && b.dB.splits > 1)
+        return fail(DORA_E_HIP, "dh, dm and dB: a split product needs fp32 slots");
+    GemmArgs a = seg1(d_out, r, dy, d_out, P, r, T);
+    a.Y = y;
+    a.dh_out = dh;
+    a.dm_part = dmpart;
+    a.dh_m = m;
+    a.dh_n = n;
+    a.mode = EPI_STORE;
+    a.splits = b.dB.splits;
+    a.steps_per_split = b.dB.sps;
+    a.out = out;
+    a.ldc = r;
+    a.out_f32 = f32;
+    a.alpha = alpha;
+    DORA_LAUNCH(launch_gemm_bf16_dhdm(a, b.dB.cfg, st), "dh, dm and dB");
     return DORA_OK;
 }
 
@@ -1352,8 +1395,19 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
     float *dmpart = reinterpret_cast<float *>(w + p.o_dmpart);
     void *Q = w + p.o_Q;
 
-    // 1. dh = g dy and dm partial sums (one pass over dy and y), then dm.
-    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, p.sweep, dh, dmpart, st), "dh/dm");
+    // 1. dh = g dy and dm partial sums (one pass over dy and y), then dm;
+    //    with the fused plan the same pass also forms dB = s dh^T P.
+    if (p.fused_dhdm) {
+        float *part = reinterpret_cast<float *>(w + p.o_dBpart);
+        const bool split = p.dB.splits > 1;
+        DORA_CHECK(run_dhdm_dB(p, dy, y, m, n, P, T, d_out, r, dh, dmpart, split ? part : dB,
+                               split ? 1 : 0, split ? 1.0f : s, st));
+        if (split)
+            DORA_LAUNCH(launch_splitk_reduce(bf, part, p.dB.splits, d_out, r, s, dB, st), "dB");
+    } else {
+        DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, p.sweep, dh, dmpart, st),
+                    "dh/dm");
+    }
     DORA_LAUNCH(launch_dm_finish(dmpart, p.nchunks, m, d_out, dm, st), "dm finish");
     // 2. Q = s dh B  (A K-major, B MN-major).
     DORA_CHECK(run_store(bf, p.q, seg1(T, r, dh, d_out, B, r, d_out), 1, Q, r, s,
@@ -1366,9 +1420,10 @@ int dora_backward(const void *dy, const void *x, const void *W, const void *A, c
         DORA_CHECK(run_store(bf, p.dx, g, 1, dx, d_in, 1.0f,
                              reinterpret_cast<float *>(w + p.o_dxpart), st, "dx"));
     }
-    // 4. dB = s dh^T P  (both MN-major, K = T).
-    DORA_CHECK(run_store(bf, p.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, dB, r, s,
-                         reinterpret_cast<float *>(w + p.o_dBpart), st, "dB"));
+    // 4. dB = s dh^T P  (both MN-major, K = T), unless formed in step 1.
+    if (!p.fused_dhdm)
+        DORA_CHECK(run_store(bf, p.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, dB, r, s,
+                             reinterpret_cast<float *>(w + p.o_dBpart), st, "dB"));
     // 5. dA = Q^T x  (both MN-major, K = T).
     DORA_CHECK(run_store(bf, p.dA, seg1(r, d_in, Q, r, x, d_in, T), 2, dA, d_in, 1.0f,
                          reinterpret_cast<float *>(w + p.o_dApart), st, "dA"));
@@ -1423,8 +1478,14 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
     float *yslots = reinterpret_cast<float *>(w + p.o_yslots);
     const size_t gsz = bf ? static_cast<size_t>(r) * r * 2 : 0;  // lo half of a hi/lo pair
 
-    // 1-3. As with n held constant: dh = g dy and dm, Q = s dh B, dx = [dh | Q] [W ; A].
-    DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, b.sweep, dh, dmpart, st), "dh/dm");
+    // 1-3. As with n held constant: dh = g dy and dm (with the fused plan the
+    //      same pass also puts s dh^T P into dB's fp32 slots), Q = s dh B,
+    //      dx = [dh | Q] [W ; A].
+    if (b.fused_dhdm)
+        DORA_CHECK(run_dhdm_dB(b, dy, y, m, n, P, T, d_out, r, dh, dmpart, bslots, 1, s, st));
+    else
+        DORA_LAUNCH(launch_dh_dm_partial(bf, dy, y, m, n, T, d_out, b.sweep, dh, dmpart, st),
+                    "dh/dm");
     DORA_LAUNCH(launch_dm_finish(dmpart, b.nchunks, m, d_out, dm, st), "dm finish");
     DORA_CHECK(run_store(bf, b.q, seg1(T, r, dh, d_out, B, r, d_out), 1, Q, r, s,
                          reinterpret_cast<float *>(w + b.o_Qpart), st, "Q = s dh B"));
@@ -1465,8 +1526,9 @@ int dora_backward_through_norm(const void *dy, const void *x, const void *W, con
     }
     // 6. dB = s dh^T P + cs (.) V A^T,  V A^T = W A^T + s B G,  G = A A^T.
     {
-        DORA_CHECK(run_slots(bf, b.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, bslots, s, st,
-                             "dB: s dh^T P"));
+        if (!b.fused_dhdm)
+            DORA_CHECK(run_slots(bf, b.dB, seg1(d_out, r, dh, d_out, P, r, T), 2, bslots, s, st,
+                                 "dB: s dh^T P"));
         // V A^T = W A^T + s B G: the norm's own product when the caller kept it
         // (U), else formed here
         if (!U) {

@@ -58,13 +58,27 @@ struct GemmArgs {
     // per-row factors)
     const float *colm;
     const float *coln;
-    // EPI_ROWDOT, EPI_MERGE
-    const void *E;
-    int64_t lde;
-    float *rowdot;
+    // EPI_ROWDOT, EPI_MERGE: E (ld lde); EPI_ROWDOT: rowdot; and an
     // optional sum of squares of A's rows over each split's K range (K-major
-    // A only; written by the tiles of the first N block): rowsq[z*M + m]
-    float *rowsq;
+    // A only; written by the tiles of the first N block): rowsq[z*M + m].
+    // dh/dm production (launch_gemm_bf16_dhdm, an EPI_STORE product) uses
+    // the same places for y in A's layout, the raw dm sums dm_part[z*M + m]
+    // and the dh output (A's layout and lda), with g_m = dh_m[m] / dh_n[m]
+    // for A's index m.
+    union {
+        const void *E;
+        const void *Y;
+    };
+    int64_t lde;
+    union {
+        float *rowdot;
+        float *dm_part;
+    };
+    union {
+        float *rowsq;
+        void *dh_out;
+    };
+    const float *dh_m, *dh_n;
 };
 
 // Up to kMaxGroup independent products in one launch (passed by value as the
@@ -91,6 +105,11 @@ static_assert(sizeof(GemmGroup) <= 4096, "a group must fit the kernel argument s
 // shape (see gemm_configs in the .hip file).
 hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs &a, int layout, bool rowsq, hipStream_t st);
+// The backward's dB = alpha dh^T P with dh = g (.) dy and the dm sums formed
+// in the same pass (both operands MN-major, one segment: a.seg[0].a = dy,
+// a.seg[0].b = P; a.Y, a.dh_out, a.dm_part, a.dh_m / a.dh_n set).  Only the
+// configurations with dhdm_ok take it.
+hipError_t launch_gemm_bf16_dhdm(const GemmArgs &a, int cfg, hipStream_t st);
 // Grouped launch of the pipelined bf16 kernel (cfg must be a direct-to-LDS
 // configuration); tile_start and count are filled in here from the problems'
 // shapes and splits.
@@ -109,6 +128,7 @@ struct TileCfg {
     bool rowsq_ok;    // row sums of squares of A supported
     bool direct_rowdot;  // EPI_ROWDOT formed from the accumulators (no LDS staging)
     bool ragged_ok;      // also takes operands of any width (element-masked loads)
+    bool dhdm_ok;        // has the dh/dm-producing variant (launch_gemm_bf16_dhdm)
 };
 int gemm_bf16_num_cfgs();
 TileCfg gemm_bf16_cfg(int cfg);

@@ -351,25 +351,25 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmArgs g)
 // The 128 x 128 register-staged configuration also exists with
 // element-masked loads (ragged_ok), for operands of any width.
 constexpr TileCfg kCfgs[] = {
-    {256, 256, GEMM_BK, false, 0.76f, true, true, false, false},
-    {256, 128, GEMM_BK, false, 0.68f, true, true, false, false},
-    {128, 128, GEMM_BK, false, 0.56f, true, true, false, true},
-    {128, 64, GEMM_BK, false, 0.40f, true, true, false, false},
+    {256, 256, GEMM_BK, false, 0.76f, true, true, false, false, false},
+    {256, 128, GEMM_BK, false, 0.68f, true, true, false, false, false},
+    {128, 128, GEMM_BK, false, 0.56f, true, true, false, true, false},
+    {128, 64, GEMM_BK, false, 0.40f, true, true, false, false, false},
     // 4 waves (2 x 2), 128 x 128 per wave
-    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false, false, false},
-    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false, false, false},  // 4 waves (2 x 2)
-    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false, false, false},  // 4 waves (2 x 2), 2 per CU
+    {256, 256, GEMM_DMA_BK, true, 1.00f, true, false, false, false, false},
+    {256, 128, GEMM_DMA_BK, true, 0.80f, true, false, false, false, false},  // 4 waves (2 x 2)
+    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false, false, false, false},  // 4 waves (2 x 2), 2 per CU
     // 4 waves (1 x 4): a whole rank-384 row block per tile, so the row-dot
     // products of the factored norm read W once, and products with N = r
     // (x A^T, dh B) read their long operand once
-    {128, 384, GEMM_DMA_BK, true, 0.77f, true, true, true, false},
+    {128, 384, GEMM_DMA_BK, true, 0.77f, true, true, true, false, false},
     // 4 waves (4 x 1): the same with M = r (Q^T x)
-    {384, 128, GEMM_DMA_BK, true, 0.77f, true, false, false, false},
+    {384, 128, GEMM_DMA_BK, true, 0.77f, true, false, false, false, false},
     // 8 waves (2 x 4, 64 x 96 per wave): the rank-384 row block with two
     // waves per SIMD, which hide each other's waits (measured on the
     // norm's row-dot products against the 4-wave tile: W A^T 231 -> 208 us,
     // B G 42 -> 28 us at d_out 28672, d_in 8192, r 384)
-    {128, 384, GEMM_DMA_BK, true, 0.85f, true, true, true, false},
+    {128, 384, GEMM_DMA_BK, true, 0.85f, true, true, true, false, true},
 };
 
 }  // namespace
@@ -467,6 +467,20 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, int layout, int cfg, bool rowsq, 
         return launch_dma_384x128(a, layout, rowsq, st);
     case 9:
         return launch_dma_128x384w8(a, layout, rowsq, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_bf16_dhdm(const GemmArgs &a, int cfg, hipStream_t st)
+{
+    if (cfg < 0 || cfg >= gemm_bf16_num_cfgs() || !kCfgs[cfg].dhdm_ok || a.nseg != 1 ||
+        a.mode != EPI_STORE || ragged_args(a, 2) || !a.Y || !a.dh_out || !a.dm_part || !a.dh_m ||
+        !a.dh_n || a.colm || a.coln)
+        return hipErrorInvalidValue;
+    switch (cfg) {
+    case 9:
+        return launch_dma_dhdm_128x384w8(a, st);
     default:
         return hipErrorInvalidValue;
     }

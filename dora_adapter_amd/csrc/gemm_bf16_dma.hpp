@@ -110,13 +110,16 @@ __device__ __forceinline__ void stage_barrier()
     __asm__ volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN>
+// DH: the A operand is produced in the kernel (the backward's dh from dy, see
+// gemm_dma_tile); a third tile per stage, of A's shape, holds y.
+template <int BM, int BN, int WM, int WN, bool DH = false>
 struct DmaCfg {
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
     static constexpr int A_BYTES = BM * ROW_BYTES;  // also [BK][BM] for MN-major
     static constexpr int B_BYTES = BN * ROW_BYTES;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int Y_BYTES = DH ? A_BYTES : 0;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + Y_BYTES;
     static constexpr int OPS = 2 * STAGE_BYTES;
     // stored epilogue: fp32 rows of the tile staged in LDS, ER at a time (a
     // wave row's BM / WM rows, or half or a quarter of them where those do
@@ -145,7 +148,7 @@ struct DmaCfg {
     // 1 KiB load instructions per operand tile and per wave and stage
     static constexpr int A_INST = A_BYTES / 1024, B_INST = B_BYTES / 1024;
     static_assert(A_INST % NW == 0 && B_INST % NW == 0, "tile loads must split over wavefronts");
-    static constexpr int LPS = (A_INST + B_INST) / NW;
+    static constexpr int LPS = (A_INST * (DH ? 2 : 1) + B_INST) / NW;
     static_assert(LPS < 64, "vmcnt range");
 };
 
@@ -241,7 +244,14 @@ struct OperandDma {
     static constexpr int PITCH = R * 2;  // MN-major row bytes
     static_assert(KMAJ || R >= 128, "MN-major tiles need >= 16 chunks per row");
     uint32_t off[PER];
-    uint32_t kch[KMAJ ? PER : 1];
+
+    // K-major: the first K index (within the stage) of the chunk lane l of
+    // wave `wave` fetches for load i (formed where a stage needs it, not kept)
+    __device__ __forceinline__ static uint32_t kchunk(int wave, int i, int lane)
+    {
+        const int rloc = (wave * PER + i) * 8 + (lane >> 3);
+        return static_cast<uint32_t>(((lane & 7) ^ swz(rloc)) * 8);
+    }
 
     __device__ __forceinline__ void init(int64_t mn_extent, int64_t ld, int64_t mn0, int wave,
                                          int lane)
@@ -256,7 +266,6 @@ struct OperandDma {
                 int64_t row = mn0 + rloc;
                 row = row < mn_extent ? row : mn_extent - 1;
                 off[i] = static_cast<uint32_t>((row * ld + chunk * 8) * 2) + bias;
-                kch[i] = static_cast<uint32_t>(chunk * 8);
             } else {
                 const int b = blk * 1024 + lane * 16;
                 const int krow = b / PITCH;
@@ -329,11 +338,23 @@ __device__ __forceinline__ void mfma_one(f32x16_t (&acc)[TM][TN], const Frags<TM
 }
 
 // One output tile (tm, tn) of split z of the product g.
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
+//
+// DH (the backward's dB = s dh^T P with dh and dm formed on the way, for A
+// = dy [K = T][M = d_out] MN-major, B = P MN-major, one segment): every stage
+// also loads the matching tile of y (g.Y, same layout as dy), and once a
+// stage has landed each thread turns two 16-byte chunks of the dy tile into
+// dh = g dy (g = dh_m / dh_n per column, rounded once to bf16) in place,
+// stores them to g.dh_out (from the tiles of the first N block) and adds
+// dy * y into its running dm sums; the MFMAs then read dh.  A thread keeps
+// one 8-column chunk of the tile for the whole K loop, so its dm sums need
+// one fixed-order reduction over the tile's threads at the end, written to
+// g.dm_part[z * M + m] (the raw sums over this split's tokens).
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ, bool DH = false>
 __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, const int tn,
                                               const int z)
 {
-    using C = DmaCfg<BM, BN, WM, WN>;
+    using C = DmaCfg<BM, BN, WM, WN, DH>;
+    static_assert(!DH || (!AK && !BKM && !ROWSQ), "dh/dm production: both operands MN-major");
     constexpr int G = group_size<(BM * ROW_BYTES / 1024) / (WM * WN),
                                  (BN * ROW_BYTES / 1024) / (WM * WN)>();
     using DA = OperandDma<AK, BM, WM * WN, G>;
@@ -343,7 +364,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold 32x32 MFMA tiles");
     static_assert(!ROWSQ || AK, "row sums of squares: K-major A");
-    static_assert(DA::PER + DB::PER == C::LPS, "load count");
+    static_assert(DA::PER * (DH ? 2 : 1) + DB::PER == C::LPS, "load count");
 
     __shared__ __align__(1024) unsigned char smem[C::SMEM];
 
@@ -364,24 +385,28 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     if (s_end > st_total)
         s_end = st_total;
 
-    // per-segment load plans and byte ranges (a K-major operand spans its M
-    // or N rows, an MN-major one its K rows)
-    DA da0, da1;
-    DB db0, db1;
-    da0.init(g.M, g.seg[0].lda, m0, wave, lane);
-    db0.init(g.N, g.seg[0].ldb, n0, wave, lane);
+    // byte ranges per segment (a K-major operand spans its M or N rows, an
+    // MN-major one its K rows), and the load plan of the segment whose
+    // stages are being loaded: every loop below loads stages of one segment
+    // only, so one plan is kept and rebuilt between loops (use_seg)
     const int na0 = range_bytes((AK ? g.M : g.seg[0].K) * g.seg[0].lda * 2);
     const int nb0 = range_bytes((BKM ? g.N : g.seg[0].K) * g.seg[0].ldb * 2);
     int na1 = na0, nb1 = nb0;
     if (g.nseg > 1) {
-        da1.init(g.M, g.seg[1].lda, m0, wave, lane);
-        db1.init(g.N, g.seg[1].ldb, n0, wave, lane);
         na1 = range_bytes((AK ? g.M : g.seg[1].K) * g.seg[1].lda * 2);
         nb1 = range_bytes((BKM ? g.N : g.seg[1].K) * g.seg[1].ldb * 2);
-    } else {
-        da1 = da0;
-        db1 = db0;
     }
+    DA da;
+    DB db;
+    int plan_seg = -1;
+    auto use_seg = [&](int q) {
+        q = q > 0 && g.nseg > 1 ? 1 : 0;
+        if (q != plan_seg) {
+            da.init(g.M, g.seg[q].lda, m0, wave, lane);
+            db.init(g.N, g.seg[q].ldb, n0, wave, lane);
+            plan_seg = q;
+        }
+    };
 
     auto slot = [&](int64_t s) {
         return smem + static_cast<int>((s - s_begin) & 1) * C::STAGE_BYTES;
@@ -415,25 +440,33 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         // most time to land: A (x, dh rows) for a K-major B, B (a weight
         // read MN-major) otherwise (measured both ways on x W^T and dh W)
         constexpr int GB = DB::PER / G;
-        const bool isa = BKM ? d < GA : d >= GB;
-        const int i0 = (isa ? (BKM ? d : d - GB) : (BKM ? d - GA : d)) * G;
+        // DH: groups past A's load the y tile (A's shape and plan)
+        const bool isy = DH && d >= GB + GA;
+        const bool isa = BKM ? d < GA : (d >= GB && !isy);
+        const int i0 = (isa ? (BKM ? d : d - GB) : isy ? d - GB - GA : (BKM ? d - GA : d)) * G;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-            reinterpret_cast<uintptr_t>((lds_void *)(slot(sd) + (isa ? 0 : C::A_BYTES) +
-                                                     (wave * (isa ? DA::PER : DB::PER) + i0) *
+            reinterpret_cast<uintptr_t>((lds_void *)(slot(sd) +
+                                                     (isa ? 0 : isy ? C::A_BYTES + C::B_BYTES
+                                                                    : C::A_BYTES) +
+                                                     (wave * (isa || isy ? DA::PER : DB::PER) +
+                                                      i0) *
                                                          1024))));
         Group grp;
         uint32_t *v = grp.v;
         uint32_t soff;
         __amdgpu_buffer_rsrc_t rs;
-        if (isa) {
-            rs = scalar_rsrc(sg1 ? g.seg[1].a : g.seg[0].a, live ? (sg1 ? na1 : na0) : 0);
+        if (isa || isy) {
+            rs = scalar_rsrc(isy ? g.Y : sg1 ? g.seg[1].a : g.seg[0].a,
+                             live ? (sg1 ? na1 : na0) : 0);
             const int64_t ld = sg1 ? g.seg[1].lda : g.seg[0].lda;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const uint32_t off = sg1 ? da1.off[i0 + j] : da0.off[i0 + j];
+                const uint32_t off = da.off[i0 + j];
                 if constexpr (AK) {
-                    const uint32_t kq = sg1 ? da1.kch[i0 + j] : da0.kch[i0 + j];
-                    v[j] = (MODE != LOAD_ANY || kd + kq < kseg) ? off : OOB_OFFSET;
+                    if constexpr (MODE == LOAD_ANY)
+                        v[j] = kd + DA::kchunk(wave, i0 + j, lane) < kseg ? off : OOB_OFFSET;
+                    else
+                        v[j] = off;
                 } else {
                     v[j] = off + static_cast<uint32_t>(kd * ld * 2);
                 }
@@ -444,10 +477,12 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             const int64_t ld = sg1 ? g.seg[1].ldb : g.seg[0].ldb;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const uint32_t off = sg1 ? db1.off[i0 + j] : db0.off[i0 + j];
+                const uint32_t off = db.off[i0 + j];
                 if constexpr (BKM) {
-                    const uint32_t kq = sg1 ? db1.kch[i0 + j] : db0.kch[i0 + j];
-                    v[j] = (MODE != LOAD_ANY || kd + kq < kseg) ? off : OOB_OFFSET;
+                    if constexpr (MODE == LOAD_ANY)
+                        v[j] = kd + DB::kchunk(wave, i0 + j, lane) < kseg ? off : OOB_OFFSET;
+                    else
+                        v[j] = off;
                 } else {
                     v[j] = off + static_cast<uint32_t>(kd * ld * 2);
                 }
@@ -508,6 +543,62 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     constexpr int NMF = 2 * TM * TN;    // MFMAs per half
     constexpr int NRD = 2 * (TM + TN);  // fragment reads per half
     using FR = Frags<TM, TN>;
+    // DH: dh = g dy in place over the landed A tile of stage sd, dh to
+    // g.dh_out, dy * y into the running dm sums.  Thread tid keeps column
+    // chunk c = tid % CPC of the tile (8 columns) and rows k = q / CPC of its
+    // chunks q = tid + j NT.
+    constexpr int CPC = DH ? BM / 8 : 1;          // 16-byte chunks per K row
+    constexpr int NCHK = DH ? BK * CPC / NT : 1;  // chunks per thread and stage
+    static_assert(!DH || (BK * CPC) % NT == 0, "dy chunks must split over threads");
+    float gcol[DH ? 8 : 1], dmacc[DH ? 8 : 1];
+    if constexpr (DH) {
+        const int64_t col0 = m0 + (tid % CPC) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            gcol[q] = col0 + q < g.M ? g.dh_m[col0 + q] / g.dh_n[col0 + q] : 0.f;
+            dmacc[q] = 0.f;
+        }
+    }
+    auto produce_dh = [&](int64_t sd) {
+        if constexpr (DH) {
+            unsigned char *At = slot(sd);
+            const unsigned char *Yt = At + C::A_BYTES + C::B_BYTES;
+            const int c = tid % CPC;
+            const int64_t col = m0 + c * 8;
+#pragma unroll
+            for (int j = 0; j < NCHK; ++j) {
+                const int k = (tid + j * NT) / CPC;
+                const int off = k * (BM * 2) + ((c ^ swz_mn(k)) << 4);
+                const uint4 dv = *reinterpret_cast<const uint4 *>(At + off);
+                const uint4 yv = *reinterpret_cast<const uint4 *>(Yt + off);
+                const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+                const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+                float h[8];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float d0 = __uint_as_float(dw[w] << 16);
+                    const float d1 = __uint_as_float(dw[w] & 0xffff0000u);
+                    const float y0 = __uint_as_float(yw[w] << 16);
+                    const float y1 = __uint_as_float(yw[w] & 0xffff0000u);
+                    dmacc[2 * w] = __fmaf_rn(d0, y0, dmacc[2 * w]);
+                    dmacc[2 * w + 1] = __fmaf_rn(d1, y1, dmacc[2 * w + 1]);
+                    h[2 * w] = gcol[2 * w] * d0;
+                    h[2 * w + 1] = gcol[2 * w + 1] * d1;
+                }
+                const uint4 hv = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
+                                            pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
+                *reinterpret_cast<uint4 *>(At + off) = hv;
+                const int64_t t = sd * BK + k;
+                if (tn == 0 && t < g.seg[0].K && col < g.M)
+                    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(g.dh_out) +
+                                               t * g.seg[0].lda + col) = hv;
+            }
+            // the dh chunks are in LDS before any wave reads fragments
+            wait_lgkm0();
+            stage_barrier();
+        }
+    };
+
     auto half = [&](auto h_c, int64_t D, FR &cur, FR &nxt, auto mode_c) {
         constexpr int H = decltype(h_c)::value;
         constexpr bool MODE_LOADS = decltype(mode_c)::value != LOAD_NONE;
@@ -522,6 +613,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             // D's fragments, so its slot takes stage D + 2
             wait_vmcnt<0>();
             stage_barrier();
+            if constexpr (DH) {
+                if (D + 1 < s_end)
+                    produce_dh(D + 1);
+            }
         }
         // half 0 reads half 1 of the same stage; half 1 reads half 0 of D + 1
         const unsigned char *An = slot(H == 0 ? D : D + 1);
@@ -564,14 +659,17 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         // prologue: stages s_begin and s_begin + 1 in flight, then s_begin
         // visible and the fragments of its half 0 read
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+        for (int p = 0; p < 2; ++p) {
+            use_seg(s_begin + p >= st1 ? 1 : 0);
 #pragma unroll
             for (int d = 0; d < NG; ++d) {
                 const Group grp = dma_prep(s_begin + p, d, std::integral_constant<int, LOAD_ANY>{});
                 static_for<G>([&](auto jc) { issue(grp, jc); });
             }
+        }
         wait_vmcnt<C::LPS>();  // stage s_begin has landed
         stage_barrier();
+        produce_dh(s_begin);
         static_for<NRD>([&](auto oc) {
             read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, decltype(oc)::value>(
                 fa, slot(s_begin), slot(s_begin) + C::A_BYTES, 0, wm, wn, lane);
@@ -596,14 +694,38 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         const int64_t b1 = clamp(lesser(st1, s_end) - 2, e0, s_end);
         const int64_t e1 = clamp(lesser(st1 + full1, s_end) - 2, b1, s_end);
         const int64_t dd = clamp(s_end - 2, e1, s_end);
+        // the first two loops load stages of segment 0, the next two of
+        // segment 1 (stages past the split's end load nothing, whatever the
+        // plan)
+        if (s_begin < b1)
+            use_seg(0);
         stages(s_begin, e0, std::integral_constant<int, LOAD_SEG0>{});
         stages(e0, b1, std::integral_constant<int, LOAD_ANY>{});
+        use_seg(1);
         stages(b1, e1, std::integral_constant<int, LOAD_SEG1>{});
         stages(e1, dd, std::integral_constant<int, LOAD_ANY>{});
         stages(dd, s_end, std::integral_constant<int, LOAD_NONE>{});
         wait_vmcnt<0>();  // the empty loads past the end have deposited their zeros
     }
     stage_barrier();  // every wave is done reading the slots before LDS is reused
+
+    if constexpr (DH) {
+        // dm: the tile's threads of one column chunk summed in a fixed order
+        constexpr int RS = NT / CPC;  // threads per column chunk
+        float *red = reinterpret_cast<float *>(smem);  // [RS][BM]
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            red[(tid / CPC) * BM + (tid % CPC) * 8 + q] = dmacc[q];
+        __syncthreads();
+        for (int col = tid; col < BM; col += NT) {
+            float sum = 0.f;
+            for (int w = 0; w < RS; ++w)
+                sum += red[w * BM + col];
+            if (tn == 0 && m0 + col < g.M)
+                g.dm_part[static_cast<int64_t>(z) * g.M + m0 + col] = sum;
+        }
+        __syncthreads();
+    }
 
     if constexpr (ROWSQ) {
         if (g.rowsq != nullptr && tn == 0) {
@@ -781,12 +903,12 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool ROWSQ, bool DH = false>
 __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_kernel(GemmArgs g)
 {
     int tm, tn;
     tile_coords(g.M, g.N, BM, BN, tm, tn);
-    gemm_dma_tile<BM, BN, WM, WN, AK, BKM, ROWSQ>(g, tm, tn, static_cast<int>(blockIdx.y));
+    gemm_dma_tile<BM, BN, WM, WN, AK, BKM, ROWSQ, DH>(g, tm, tn, static_cast<int>(blockIdx.y));
 }
 
 // Several independent products in one launch (one tile configuration and

@@ -1,8 +1,9 @@
 // gemm_dma_cfg.hip - one tile configuration of the pipelined bf16 GEMM:
 // its kernels (single product and grouped launch, every operand layout) and
-// their launchers.  Compiled once per configuration with DORA_DMA_CFG = 0..6
+// their launchers.  Compiled once per configuration with DORA_DMA_CFG = 0..7
 // (256 x 256, 256 x 128, 128 x 128, 128 x 384, 384 x 128; 5: the 128 x 384
-// kernels that also sum squares of rows; 6: the other grouped 128 x 384 ones).
+// kernels that also sum squares of rows; 6: the other grouped 128 x 384 ones;
+// 7: 128 x 384 with eight waves).
 #include "gemm_dma_launch.hpp"
 
 #ifndef DORA_DMA_CFG
@@ -93,6 +94,13 @@ hipError_t launch_dma_128x384w8(const GemmArgs &a, int layout, bool rowsq, hipSt
 hipError_t launch_dma_group_128x384w8(GemmGroup &g, int layout, bool rowsq, hipStream_t st)
 {
     return dma::launch_dma_group_layout<128, 384, 2, 4>(g, layout, rowsq, st);
+}
+// dB with dh and the dm sums produced on the way (both operands MN-major)
+template __global__ void dma::gemm_bf16_dma_kernel<128, 384, 2, 4, false, false, false, true>(
+    GemmArgs);
+hipError_t launch_dma_dhdm_128x384w8(const GemmArgs &a, hipStream_t st)
+{
+    return dma::launch_dma<128, 384, 2, 4, false, false, false, true>(a, st);
 }
 #else
 #error "DORA_DMA_CFG out of range"

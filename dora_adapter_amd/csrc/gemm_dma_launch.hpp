@@ -9,14 +9,14 @@
 namespace dora {
 namespace dma {
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool RS, bool DH = false>
 hipError_t launch_dma(const GemmArgs &a, hipStream_t st)
 {
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles == 0 || a.splits == 0)
         return hipSuccess;
     dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.splits));
-    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, AK, BKM, RS>), grid,
+    hipLaunchKernelGGL((dma::gemm_bf16_dma_kernel<BM, BN, WM, WN, AK, BKM, RS, DH>), grid,
                        dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
 }
@@ -97,5 +97,6 @@ DORA_DMA_LAUNCHERS(128, 384)
 DORA_DMA_LAUNCHERS(384, 128)
 DORA_DMA_LAUNCHERS(128, 384w8)
 #undef DORA_DMA_LAUNCHERS
+hipError_t launch_dma_dhdm_128x384w8(const GemmArgs &a, hipStream_t st);
 
 }  // namespace dora
