@@ -559,6 +559,28 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             dmacc[q] = 0.f;
         }
     }
+    // The dh chunks of the stage last produced go to g.dh_out as buffer
+    // stores issued after that half's loads (flush_dh, which reads them back
+    // from the stage's slot, untouched until the next half 1's loads): a
+    // wave's memory operations retire in issue order, so the next stage's
+    // wait for its loads can leave those NCHK stores in flight
+    // (wait_vmcnt<NCHK>) instead of waiting for the writes too.  Lanes with
+    // nothing to store (past T, past M, tiles of other N blocks, stages past
+    // the split) store to an offset outside the descriptor's range, which the
+    // hardware drops, so every wave issues the same NCHK stores each time.
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    uint32_t dh_off[NCHK];
+    int64_t dh_sd = 0;  // the stage whose dh chunks flush_dh stores
+    __amdgpu_buffer_rsrc_t dh_rs;
+    if constexpr (DH) {
+        const int64_t dh_bytes = tn == 0 ? g.seg[0].K * g.seg[0].lda * 2 : 0;
+        dh_rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void *>(g.dh_out), static_cast<short>(0),
+            __builtin_amdgcn_readfirstlane(static_cast<int>(dh_bytes)), 0x00020000);
+#pragma unroll
+        for (int j = 0; j < NCHK; ++j)
+            dh_off[j] = OOB_OFFSET;
+    }
     auto produce_dh = [&](int64_t sd) {
         if constexpr (DH) {
             unsigned char *At = slot(sd);
@@ -589,13 +611,30 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                                             pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
                 *reinterpret_cast<uint4 *>(At + off) = hv;
                 const int64_t t = sd * BK + k;
-                if (tn == 0 && t < g.seg[0].K && col < g.M)
-                    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(g.dh_out) +
-                                               t * g.seg[0].lda + col) = hv;
+                dh_off[j] = t < g.seg[0].K && col < g.M
+                                ? static_cast<uint32_t>((t * g.seg[0].lda + col) * 2)
+                                : OOB_OFFSET;
             }
+            dh_sd = sd;
             // the dh chunks are in LDS before any wave reads fragments
             wait_lgkm0();
             stage_barrier();
+        }
+    };
+    auto flush_dh = [&]() {
+        if constexpr (DH) {
+            const unsigned char *At = slot(dh_sd);
+            const int c = tid % CPC;
+#pragma unroll
+            for (int j = 0; j < NCHK; ++j) {
+                const int k = (tid + j * NT) / CPC;
+                const uint4 hv = *reinterpret_cast<const uint4 *>(At + k * (BM * 2) +
+                                                                  ((c ^ swz_mn(k)) << 4));
+                const i32x4_t v = {static_cast<int>(hv.x), static_cast<int>(hv.y),
+                                   static_cast<int>(hv.z), static_cast<int>(hv.w)};
+                __builtin_amdgcn_raw_buffer_store_b128(v, dh_rs, dh_off[j], 0, 0);
+                dh_off[j] = OOB_OFFSET;  // a later flush before another stage is produced drops
+            }
         }
     };
 
@@ -611,7 +650,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             // stage D + 1 has landed (it is the only one in flight); after
             // the barrier it is visible and every wave holds all of stage
             // D's fragments, so its slot takes stage D + 2
-            wait_vmcnt<0>();
+            // (DH: the newest NCHK operations are the previous stage's dh
+            // stores, which may stay in flight)
+            wait_vmcnt<DH ? NCHK : 0>();
             stage_barrier();
             if constexpr (DH) {
                 if (D + 1 < s_end)
@@ -652,6 +693,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             });
             __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (H == 1)
+            flush_dh();  // after this half's loads
     };
 
     FR fa, fb;  // half 0 and half 1 of a stage
@@ -670,6 +713,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
         wait_vmcnt<C::LPS>();  // stage s_begin has landed
         stage_barrier();
         produce_dh(s_begin);
+        flush_dh();
         static_for<NRD>([&](auto oc) {
             read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, decltype(oc)::value>(
                 fa, slot(s_begin), slot(s_begin) + C::A_BYTES, 0, wm, wn, lane);
