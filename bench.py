@@ -36,8 +36,11 @@ Printed JSON line (one):
   stream_ceiling  the best rate over the launch shapes of a plain two-in /
                one-out 16-byte non-temporal stream of the same size, MALL
                flushed: the ceiling the compose and dh/dm are held against.
-  dh_dm_*      (c5) the backward's dh = g dy and dm pass from the profiler's
-               device trace, 6 bytes per bf16 element.
+  dh_dm_*      (c5) the backward's dh = g dy and dm: dh_dm_dB_us the dB
+               product that forms them on the way (the step's path) and its
+               rate over the dy, y, dh streams; dh_dm_us / dh_dm_GBps the
+               separate streaming pass (6 bytes per bf16 element), from one
+               backward with the planners restricted to another tile shape.
   step_kernels_us  (c5) every kernel of one forward + backward step, in
                launch order, from the profiler's device trace.
   merge_*, bwd_through_norm_*, group_norm, group_forward_qkv  (c5) the
@@ -73,6 +76,7 @@ KERNEL_WARMUP = 10  # untimed launches before each kernel-leg burst (the clock s
 GROUP_LAYERS = 8   # decoder layers whose 7 projections form the grouped-norm workload
 CONFIGS = ("c2", "c3", "c4", "c5")
 NORM_KERNELS = ("gram_AAt", "gram_finalize", "U_WAt_rowdot", "BG_rowdot", "finish")
+NORM_KERNELS_G_IN_U = ("U_WAt_rowdot", "BG_rowdot", "finish")  # G's tiles beside U's
 
 
 def log(*a):
@@ -195,16 +199,17 @@ def short_name(name):
 
 
 def norm_split(torch, fn, calls=5):
-    """The factored norm's five kernels (G = A A^T, its finalize, U = W A^T
-    with the row sums and dots, B G with the row dots, the finish), averaged
-    over `calls` calls, or None if the trace does not show five per call."""
+    """The factored norm's kernels averaged over `calls` calls: five (G =
+    A A^T, its finalize, U = W A^T with the row sums and dots, B G with the
+    row dots, the finish), or three where G's tiles run in U's launch (U and
+    G together, B G, the finish); None if the trace shows neither."""
     ks = device_kernels(torch, fn, calls)
-    if len(ks) != 5 * calls:
-        return None
-    out = {}
-    for i, key in enumerate(NORM_KERNELS):
-        out[key] = round(sum(ks[5 * c + i][1] for c in range(calls)) / calls, 1)
-    return out
+    for names in (NORM_KERNELS, NORM_KERNELS_G_IN_U):
+        k = len(names)
+        if len(ks) == k * calls:
+            return {key: round(sum(ks[k * c + i][1] for c in range(calls)) / calls, 1)
+                    for i, key in enumerate(names)}
+    return None
 
 
 class StreamCeiling:
@@ -486,6 +491,7 @@ def kernel_legs(args, out, torch, D, synth, dev, timer, shapes, mods, bufs, fwd,
         split = norm_split(torch, call)
         if split:
             rec["kernels_us"] = split
+            rec["gram_tiles_in_U_launch"] = "gram_AAt" not in split
             u_flops = 2 * sh.d_out * sh.d_in * sh.r
             rec["U_mfma_util"] = round(u_flops / split["U_WAt_rowdot"] / 1e6 / PEAK_BF16_TFLOPS, 4)
             # the norm's HBM-bound floor: W, A, B read once
@@ -563,10 +569,27 @@ def c5_legs(out, torch, D, synth, dev, timer, sh, md, b, fwd, bwd, dy, grads, n2
     # every kernel of one step, from the device trace
     ks = device_kernels(torch, lambda: (fwd(), bwd()))
     out["step_kernels_us"] = [[short_name(nm), round(us, 1)] for nm, us in ks]
-    dhdm = [us for nm, us in ks if "dh_dm" in nm]
-    if dhdm:
-        out["dh_dm_us"] = round(dhdm[0], 1)
-        out["dh_dm_GBps"] = round(6 * T * d_out / dhdm[0] / 1e3, 1)
+    # dh = g dy and dm: in the step, formed inside the dB product (the
+    # kernel whose last template flag is set); its rate over the dy, y, dh
+    # streams (6 bytes per element) beside the separate pass the library
+    # runs where that product cannot (timed here by restricting the planners
+    # to another tile configuration for one backward)
+    fused = [us for nm, us in ks if nm.replace(" ", "").endswith("true>(dora::GemmArgs)")
+             and "false,false,false,true" in nm.replace(" ", "")]
+    if fused:
+        out["dh_dm_dB_us"] = round(fused[0], 1)
+        out["dh_dm_dB_stream_GBps"] = round(6 * T * d_out / fused[0] / 1e3, 1)
+    os.environ["DORA_TILE_CFG"] = "4"
+    try:
+        # (that plan's workspace differs: the binding sizes one per call)
+        ks2 = device_kernels(torch, lambda: D.dora_backward(
+            dy, x, md["W"], md["A"], md["B"], md["m"], b["n"], s, b["P"], b["y"], out=grads))
+    finally:
+        os.environ.pop("DORA_TILE_CFG", None)
+    sep = [us for nm, us in ks2 if "dh_dm" in nm]
+    if sep:
+        out["dh_dm_us"] = round(sep[0], 1)
+        out["dh_dm_GBps"] = round(6 * T * d_out / sep[0] / 1e3, 1)
 
     # merged weight for inference (norm given): read W, write W', 2 x 2 bytes per weight
     w_out = torch.empty_like(md["W"])

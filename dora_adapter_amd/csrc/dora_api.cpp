@@ -225,6 +225,10 @@ struct Carve {
 
 struct NormPlan {
     GPlan g, u, bg;
+    // G = A A^T as extra tiles of the U = W A^T launch (one wave of
+    // workgroups with room beside U's tiles, U unsplit): G's tiles take as
+    // long as U's (the same K) and write G_hi / G_lo themselves
+    bool g_with_u = false;
     size_t o_gpart, o_gfin, o_base, o_cross, o_gram;
     size_t bytes;
 };
@@ -240,6 +244,16 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, Carve &cv)
     GemmShape bgs{d_out, r, {r, r}, bf ? 2 : 1, 1, dma_operand(d_out, r) && dma_mn_operand(r, r)};
     bgs.rowdot = true;
     p.bg = plan_gemm(bf, bgs, d_out);
+    if (bf && p.u.splits == 1 && gemm_bf16_cfg(p.u.cfg).dma && gemm_bf16_cfg(p.u.cfg).store_ok) {
+        const TileCfg t = gemm_bf16_cfg(p.u.cfg);
+        const int64_t tu = ((d_out + t.BM - 1) / t.BM) * ((r + t.BN - 1) / t.BN);
+        const int64_t tg = ((r + t.BM - 1) / t.BM) * ((r + t.BN - 1) / t.BN);
+        if (tu + tg <= kCUs && dma_operand(r, d_in)) {
+            p.g_with_u = true;
+            p.g = p.u;
+            p.g.ntn = static_cast<int>((r + t.BN - 1) / t.BN);
+        }
+    }
     const size_t start = cv.off;
     p.o_gpart = cv.take(static_cast<size_t>(p.g.splits) * r * r * 4);
     p.o_gfin = cv.take(bf ? 2 * r * r * 2 : r * r * 4);
@@ -642,14 +656,22 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
     float *cpart = reinterpret_cast<float *>(ws + p.o_cross);
     float *gmpart = reinterpret_cast<float *>(ws + p.o_gram);
 
-    // G = A A^T, split-K partials, then a fixed-order sum (+ hi/lo split for bf16).
-    {
-        GemmArgs g = seg1(r, r, A, d_in, A, d_in, d_in);
-        g.mode = EPI_STORE;
-        g.out = gpart;
-        g.ldc = r;
-        g.out_f32 = 1;
-        DORA_LAUNCH(run_gemm(bf, p.g, g, 0, false, st), "gram A A^T");
+    // G = A A^T, split-K partials, then a fixed-order sum (+ hi/lo split for
+    // bf16); or, beside U's tiles, unsplit tiles writing G_hi and G_lo.
+    GemmArgs gg = seg1(r, r, A, d_in, A, d_in, d_in);
+    gg.mode = EPI_STORE;
+    gg.ldc = r;
+    if (p.g_with_u) {
+        gg.out = gfin;
+        gg.out_f32 = 0;
+        gg.out2 = static_cast<uint16_t *>(gfin) + r * r;
+        gg.out2_lo = 1;
+        gg.splits = 1;
+        gg.steps_per_split = p.g.sps;
+    } else {
+        gg.out = gpart;
+        gg.out_f32 = 1;
+        DORA_LAUNCH(run_gemm(bf, p.g, gg, 0, false, st), "gram A A^T");
         DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, gfin, st), "gram finalize");
     }
     // U = W A^T never leaves the tile: cross partials = rowdot(U_tile, B_tile),
@@ -666,7 +688,19 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
             g.out = U_out;
             g.ldc = r;
         }
-        DORA_LAUNCH(run_gemm(bf, p.u, g, 0, true, st), "cross W A^T");
+        if (p.g_with_u) {
+            // one launch: U's tiles, then G's
+            GemmGroup grp;
+            memset(&grp, 0, sizeof grp);
+            grp.count = 2;
+            grp.p[0] = g;
+            grp.p[0].splits = p.u.splits;
+            grp.p[0].steps_per_split = p.u.sps;
+            grp.p[1] = gg;
+            DORA_LAUNCH(launch_gemm_bf16_grouped(grp, 0, p.u.cfg, true, st), "cross W A^T, gram A A^T");
+        } else {
+            DORA_LAUNCH(run_gemm(bf, p.u, g, 0, true, st), "cross W A^T");
+        }
         if (U_out && p.u.splits > 1) {
             // a split product has only partial U tiles: form U once more,
             // unsplit (no workspace), as a plain fp32 product

@@ -49,9 +49,12 @@ struct GemmArgs {
     float alpha;
     // EPI_STORE, unsplit only: an optional second output of the same type,
     // layout and ldc receiving alpha2 * C, rounded once (the forward's P and
-    // s P from one accumulator)
+    // s P from one accumulator); with out2_lo (bf16 only) it receives instead
+    // the rounding residual C - bf16(C) of the first output, rounded to bf16
+    // (the Gram matrix's hi / lo pair)
     void *out2;
     float alpha2;
+    int out2_lo;
     // optional per-column magnitude scale of the store: with colm and coln
     // set, column n of alpha * C is stored as h + ((colm[n] - coln[n]) /
     // coln[n]) h, i.e. (m/n) h in the cancellation-safe form (EPI_MERGE:

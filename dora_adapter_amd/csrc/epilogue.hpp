@@ -165,10 +165,12 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
                 store_row8(static_cast<TE *>(g.out) + m * g.ldc + n, v, cnt);
             }
             if (g.out2 != nullptr) {
-                // the second output: alpha2 * C, rounded once
+                // the second output: alpha2 * C rounded once, or the residual
+                // of the first output's rounding
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
-                    v[q] = g.alpha2 * Cs[row * CST + c * 8 + q];
+                    v[q] = g.out2_lo ? v[q] - bf16_to_f32(f32_to_bf16(v[q]))
+                                     : g.alpha2 * Cs[row * CST + c * 8 + q];
                 if (g.out_f32)
                     store_row8(static_cast<float *>(g.out2) + m * g.ldc + n, v, cnt);
                 else
