@@ -120,6 +120,13 @@ __global__ void __launch_bounds__(EW_THREADS)
         return;
     const int64_t i0 = c * 8;
     const int cnt = (d_out - i0) < 8 ? static_cast<int>(d_out - i0) : 8;
+    // the first row's loads go out before the factors are formed, so their
+    // latency covers that arithmetic
+    float b0[8], l0[8];
+    if (VEC) {
+        Vec8<T>::load(base + t0 * d_out + i0, b0);
+        Vec8<T>::load(lora + t0 * d_out + i0, l0);
+    }
     // per-column factors, once per thread, each rounded once to fp32 from
     // fp64 (g - 1 = (m - n) / n and g s = m s / n): the lora term then
     // carries two roundings (g s, its product with lora) instead of three
@@ -133,7 +140,14 @@ __global__ void __launch_bounds__(EW_THREADS)
     }
     // y may be base itself: each element is read, then written, by the same
     // thread
-    for (int64_t t = t0; t < Tn; t += R) {
+    if (VEC) {
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            o[q] = compose1(b0[q], l0[q], gm1[q], gs[q]);
+        Vec8<T>::store(y + t0 * d_out + i0, o);
+    }
+    for (int64_t t = VEC ? t0 + R : t0; t < Tn; t += R) {
         const int64_t off = t * d_out + i0;
         if (VEC) {
             float b[8], l[8], o[8];
