@@ -1,9 +1,9 @@
 // gemm_dma_cfg.hip - one tile configuration of the pipelined bf16 GEMM:
 // its kernels (single product and grouped launch, every operand layout) and
 // their launchers.  Compiled once per configuration with DORA_DMA_CFG = 0..7
-// (256 x 256, 256 x 128, 128 x 128, 128 x 384, 384 x 128; 5: the 128 x 384
-// kernels that also sum squares of rows; 6: the other grouped 128 x 384 ones;
-// 7: 128 x 384 with eight waves).
+// (256 x 256 with its persistent kernels, 256 x 128, 128 x 128, 128 x 384,
+// 384 x 128; 5: the 128 x 384 kernels that also sum squares of rows; 6: the
+// other grouped 128 x 384 ones; 7: 128 x 384 with eight waves).
 #include "gemm_dma_launch.hpp"
 
 #ifndef DORA_DMA_CFG
@@ -37,6 +37,8 @@ namespace dora {
 
 #if DORA_DMA_CFG == 0
 DORA_DMA_CONFIG(256, 256, 2, 2)
+template __global__ void dma::gemm_bf16_dma_persistent_kernel<256, 256, 2, 2, true>(GemmArgs);
+template __global__ void dma::gemm_bf16_dma_persistent_kernel<256, 256, 2, 2, false>(GemmArgs);
 #elif DORA_DMA_CFG == 1
 DORA_DMA_CONFIG(256, 128, 2, 2)
 #elif DORA_DMA_CFG == 2
