@@ -142,8 +142,9 @@ int forced_tile_cfg()
 // Choose the tile configuration and the split-K count by a small time
 // model: (256-CU waves) x (one workgroup's MFMA or VALU time), plus, for a
 // split, writing and re-reading `part_per_split` fp32 values per split and
-// one extra launch.  A split keeps at least 512 K values and its partials
-// under 1 GiB.
+// one extra launch.  A split keeps at least 512 K values (128 for row-dot
+// products, whose partials are one value per row and tile column) and its
+// partials under 1 GiB.
 GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split, int only = -1)
 {
     const double cu_flops = bf16 ? 4.0e12 : 157.3e12 / kCUs * 0.5;
@@ -181,8 +182,9 @@ GPlan plan_gemm(bool bf16, const GemmShape &sh, int64_t part_per_split, int only
         for (int q = 0; q < sh.nseg; ++q)
             steps += (sh.K[q] + bk - 1) / bk;
         const int64_t tiles = ((sh.M + BM - 1) / BM) * ((sh.N + BN - 1) / BN);
-        // a split keeps at least 512 K values
-        const int64_t zmax = std::min<int64_t>(32, std::max<int64_t>(steps * bk / 512, 1));
+        // a split keeps at least 512 K values (128 for a row-dot product)
+        const int64_t kmin = sh.rowdot ? 128 : 512;
+        const int64_t zmax = std::min<int64_t>(32, std::max<int64_t>(steps * bk / kmin, 1));
         for (int64_t z = 1; z <= zmax; ++z) {
             if (z > 1 && static_cast<double>(z) * part_per_split * 4.0 > (1LL << 30))
                 break;
