@@ -886,7 +886,9 @@ GroupGemm plan_group(const std::vector<GemmShape> &sh, bool split)
             int64_t steps = 0;
             for (int k = 0; k < q.nseg; ++k)
                 steps += (q.K[k] + t.bk - 1) / t.bk;
-            zmax = std::min<int64_t>(zmax, std::max<int64_t>(steps * t.bk / 512, 1));
+            // as in plan_gemm: 512 K values per split, 128 for a row-dot product
+            zmax = std::min<int64_t>(zmax,
+                                     std::max<int64_t>(steps * t.bk / (q.rowdot ? 128 : 512), 1));
         }
         if (!ok)
             continue;
