@@ -9,7 +9,7 @@
 // one-tile-per-workgroup launch disappears.
 //
 // The epilogue runs per wave, without workgroup barriers, while the next
-// tile's first two stages are in flight:
+// tile's second stage is in flight (its first has landed):
 //   * the MFMAs take the B fragment as their first operand and A as their
 //     second, so each 32 x 32 accumulator block holds the transposed
 //     product: lane l owns output row l & 31 and, for q = 0..3, the four
