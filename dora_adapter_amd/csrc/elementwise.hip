@@ -21,12 +21,17 @@ namespace dora {
 namespace {
 
 constexpr int EW_THREADS = 256;
-// The two-in / one-out streams (compose, dh / dm) run 2^18 threads, about a
-// quarter million 16-byte vectors in flight per sweep: the launch shape at
-// which a plain stream of this pattern moves the most bytes at every
-// workload size measured (4096 x 4096 to 16384 x 27648 bf16: 5.0 - 5.9 TB/s
-// with the MALL flushed, against 4.4 - 5.6 at 2^20 threads).
-constexpr int64_t STREAM_THREADS = int64_t(1) << 18;
+// The two-in / one-out streams (compose, dh / dm) run between 2^17 and 2^18
+// threads: enough that a thread streams at least 64 rows of its column group
+// (the per-column factors it forms once, in fp64, are then paid for over
+// that many rows), up to the launch size at which a plain stream of this
+// pattern moves the most bytes (4096 x 4096 to 16384 x 27648 bf16: 5.0 - 5.9
+// TB/s with the MALL flushed, against 4.4 - 5.6 at 2^20 threads).  Measured
+// on the compose: 2^17 threads 6 - 10% faster than 2^18 at 4096^2 and 8192^2
+// (16 and 64 rows a thread), 2^18 7% faster at 8192 x 28672 (112 rows).
+constexpr int64_t STREAM_THREADS_MIN = int64_t(1) << 17;
+constexpr int64_t STREAM_THREADS_MAX = int64_t(1) << 18;
+constexpr int64_t STREAM_ROWS_PER_THREAD = 64;
 
 // 16-byte streaming accesses with the nontemporal hint: data read or written
 // once per launch should not displace what other waves still reuse (about
@@ -93,7 +98,10 @@ struct Vec8<float> {
 // streamed in address order).
 __host__ __device__ inline int64_t sweep_rows(int64_t T, int64_t gpr)
 {
-    int64_t R = (STREAM_THREADS + gpr / 2) / (gpr > 0 ? gpr : 1);
+    int64_t th = gpr * T / STREAM_ROWS_PER_THREAD;
+    th = th < STREAM_THREADS_MIN ? STREAM_THREADS_MIN
+                                 : (th > STREAM_THREADS_MAX ? STREAM_THREADS_MAX : th);
+    int64_t R = (th + gpr / 2) / (gpr > 0 ? gpr : 1);
     if (R < 1)
         R = 1;
     if (R > T)

@@ -3,8 +3,8 @@ y = (m/n)(base + s*lora), including the near-unity regime where g = m/n is
 within 1e-6 .. 1e-2 of one.
 
 A thread of the compose kernel streams one 8-column group down every R-th
-row from its first (the grid sweeps R whole rows at a time, R about 2^18
-threads over the column groups).  The large cases below make R not divide T,
+row from its first (the grid sweeps R whole rows at a time: between 2^17 and
+2^18 threads, about T / 64 per column group, over the column groups).  The large cases below make R not divide T,
 so the last sweep is partial and threads take different row counts (at the
 benchmarked 8192 x 28672 output R = 73: 112 or 113 rows per thread), in
 place and out of place."""
@@ -111,15 +111,17 @@ def test_compose_deterministic():
     assert torch.equal(a, b)
 
 
-def _sweep_rows(T, d_out, threads=1 << 18):
-    """Rows per sweep of the compose launch (2^18 threads over the column groups)."""
+def _sweep_rows(T, d_out):
+    """Rows per sweep of the compose launch: gpr T / 64 threads over the gpr
+    column groups, within [2^17, 2^18] threads."""
     gpr = (d_out + 7) // 8
+    threads = min(max(gpr * T // 64, 1 << 17), 1 << 18)
     return max(min((threads + gpr // 2) // gpr, T), 1)
 
 
 @pytest.mark.parametrize("T,d_out,dtype,rows", [
-    (4100, 8192, torch.bfloat16, 256),    # 16 whole sweeps and 4 rows
-    (4100, 16384, torch.float32, 128),    # 32 whole sweeps and 4 rows, fp32
+    (4100, 8192, torch.bfloat16, 128),    # 32 whole sweeps and 4 rows
+    (4100, 16384, torch.float32, 64),     # 64 whole sweeps and 4 rows, fp32
 ])
 @pytest.mark.parametrize("in_place", [False, True])
 def test_compose_sweeps_full(T, d_out, dtype, rows, in_place):
