@@ -235,7 +235,11 @@ constexpr int LOAD_ANY = 0, LOAD_SEG0 = 1, LOAD_SEG1 = 2, LOAD_NONE = 3;
 //   tile; lane l fetches the chunk that belongs at byte 16 l.  A stage adds
 //   k0 * ld * 2 to the per-lane offset (rows past K are out of range and
 //   load as zeros).
-template <bool KMAJ, int R, int NW, int G = GROUP>
+// SW16: the MN-major chunk swizzle of the 16 x 16 x 32 MFMA fragments
+// (swz_mn16 in gemm_persistent.hpp).
+__device__ __forceinline__ int swz_mn16(int k) { return swz_mn(k) ^ (((k >> 3) & 1) << 1); }
+
+template <bool KMAJ, int R, int NW, int G = GROUP, bool SW16 = false>
 struct OperandDma {
     static constexpr int NINST = R * ROW_BYTES / 1024;
     static_assert(NINST % NW == 0, "tile loads must split over wavefronts");
@@ -269,7 +273,7 @@ struct OperandDma {
             } else {
                 const int b = blk * 1024 + lane * 16;
                 const int krow = b / PITCH;
-                const int chunk = ((b % PITCH) >> 4) ^ swz_mn(krow);
+                const int chunk = ((b % PITCH) >> 4) ^ (SW16 ? swz_mn16(krow) : swz_mn(krow));
                 int64_t col = mn0 + chunk * 8;
                 col = col + 8 <= mn_extent ? col : mn_extent - 8;
                 off[i] = static_cast<uint32_t>((krow * ld + col) * 2) + bias;

@@ -8,13 +8,14 @@
 // pipeline never drains between tiles and the per-tile fill of a
 // one-tile-per-workgroup launch disappears.
 //
-// The epilogue runs per wave, without workgroup barriers, while the next
-// tile's second stage is in flight (its first has landed):
+// Its MFMAs are the 16 x 16 x 32 form (see read_frag16).  The epilogue runs
+// per wave, without workgroup barriers, while the next tile's second stage
+// is in flight (its first has landed):
 //   * the MFMAs take the B fragment as their first operand and A as their
-//     second, so each 32 x 32 accumulator block holds the transposed
-//     product: lane l owns output row l & 31 and, for q = 0..3, the four
-//     consecutive columns 8 q + 4 (l >> 5) + 0..3 -- after the fp32 -> bf16
-//     rounding, eight bytes of one row;
+//     second, so each 16 x 16 accumulator block holds the transposed
+//     product: lane l owns output row l & 15 and the four consecutive
+//     columns 4 (l >> 4) + 0..3 -- after the fp32 -> bf16 rounding, eight
+//     bytes of one row;
 //   * a wave rounds 32 rows x 64 columns at a time into its own 4 KiB LDS
 //     staging area (8-byte writes), reads them back as 16-byte row chunks
 //     and stores 8 rows x 128 bytes per instruction (whole cache lines);
@@ -32,13 +33,75 @@
 namespace dora {
 namespace dma {
 
-// MFMA number q of a half with the operands exchanged (acc holds the
-// transposed block).
-template <int TM, int TN, int Q>
-__device__ __forceinline__ void mfma_one_t(f32x16_t (&acc)[TM][TN], const Frags<TM, TN> &f)
+// The products run on v_mfma_f32_16x16x32_bf16: at the same matrix-core
+// occupancy it draws less power per flop than the 32 x 32 x 16 form, so the
+// part holds a higher clock under its power limit (measured from registers
+// alone: 2.04 against 1.82 GHz, both 99% busy; x W^T at 8192 x 28672 x 8192
+// 2.69 -> 2.54 ms).  A half stage (32 K values) is one K slice: lane l of a
+// fragment holds index mn + (l & 15) and the 8 K values 32 h + 8 (l >> 4) +
+// 0..7; the MFMAs take the B fragment as their first operand, so lane l of
+// an accumulator block holds output row l & 15 and the four consecutive
+// columns 4 (l >> 4) + 0..3.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int TM, int TN>
+struct Frags16 {
+    bf16x8_t a[TM], b[TN];
+};
+
+__device__ __forceinline__ bf16x8_t read_frag16(const unsigned char *tile, int mn, int h, int lane)
 {
-    constexpr int kk = Q / (TM * TN), i = (Q / TN) % TM, j = Q % TN;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j], 0, 0, 0);
+    const int row = mn + (lane & 15);
+    const int fc = 4 * h + (lane >> 4);
+    return *reinterpret_cast<const bf16x8_t *>(tile + row * ROW_BYTES + ((fc ^ swz(row)) << 4));
+}
+
+// The same fragment from an MN-major tile ([64 K rows][R], 16-byte chunk c
+// of row k at c ^ swz_mn16(k)): two ds_read_b64_tr_b16, each giving the
+// lanes of 16-lane group g the 16 columns from mn of 4 of their 8 rows.
+// Groups 0 and 1 (and 2 and 3) read rows 8 apart at the same columns;
+// swz_mn16 moves rows with bit 3 set by two chunks, so that the two groups'
+// 4 rows x 32 bytes fall on distinct banks.
+template <int R>
+__device__ __forceinline__ bf16x8_t read_frag16_mn(const unsigned char *tile, int mn, int h,
+                                                   int lane)
+{
+    constexpr int PITCH = R * 2;
+    const int grp = lane >> 4, j = lane & 15;
+    const int col = mn + 4 * (j & 3);
+    const int k = 32 * h + 8 * grp + (j >> 2);
+    const int k2 = k + 4;
+    const unsigned char *p0 =
+        tile + k * PITCH + (((col >> 3) ^ swz_mn16(k)) << 4) + ((col & 7) << 1);
+    const unsigned char *p1 =
+        tile + k2 * PITCH + (((col >> 3) ^ swz_mn16(k2)) << 4) + ((col & 7) << 1);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
+    const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Fragment read number O of half `h` (A fragments, then B; B K-major or
+// MN-major).
+template <bool BKM, int BN, int TM, int TN, int WTM, int WTN, int O>
+__device__ __forceinline__ void read_one16(Frags16<TM, TN> &f, const unsigned char *As,
+                                           const unsigned char *Bs, int h, int wm, int wn,
+                                           int lane)
+{
+    if constexpr (O < TM)
+        f.a[O] = read_frag16(As, wm * WTM + O * 16, h, lane);
+    else if constexpr (BKM)
+        f.b[O - TM] = read_frag16(Bs, wn * WTN + (O - TM) * 16, h, lane);
+    else
+        f.b[O - TM] = read_frag16_mn<BN>(Bs, wn * WTN + (O - TM) * 16, h, lane);
+}
+
+// MFMA number Q of a half (B fragment first: acc holds the transposed block).
+template <int TM, int TN, int Q>
+__device__ __forceinline__ void mfma_one16(f32x4_t (&acc)[TM][TN], const Frags16<TM, TN> &f)
+{
+    constexpr int i = Q / TN, j = Q % TN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // One direct-to-LDS load with a zero scalar offset, for loads issued outside
@@ -68,10 +131,10 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
     constexpr int G = group_size<(BM * ROW_BYTES / 1024) / (WM * WN),
                                  (BN * ROW_BYTES / 1024) / (WM * WN)>();
     using DA = OperandDma<AK, BM, WM * WN, G>;
-    using DB = OperandDma<BKM, BN, WM * WN, G>;
+    using DB = OperandDma<BKM, BN, WM * WN, G, !BKM>;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int TM = WTM / 16, TN = WTN / 16;  // 16 x 16 accumulator blocks
     static_assert(BN == 256 && WTN == 128 && NW >= 2, "m / n and staging layout");
     static_assert(DA::PER + DB::PER == C::LPS, "load count");
     constexpr int WAVE_OFF = C::OPS + 2 * PST_MN_BYTES;
@@ -219,10 +282,17 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
         lds_dma16<J>(grp.rs, grp.v[J], grp.soff);
     };
 
-    constexpr int NMF = 2 * TM * TN;
-    constexpr int NRD = 2 * (TM + TN);
-    using FR = Frags<TM, TN>;
-    using ACC = f32x16_t[TM][TN];
+    constexpr int NMF = TM * TN;  // MFMAs per half stage
+    constexpr int NRD = TM + TN;  // fragment reads per half stage
+    using FR = Frags16<TM, TN>;
+    using ACC = f32x4_t[TM][TN];
+    // fragment read O of half h, MFMA Q of a half
+    auto read_op = [&](FR &f, const unsigned char *As, const unsigned char *Bs, int h, auto o_c) {
+        read_one16<BKM, BN, TM, TN, WTM, WTN, decltype(o_c)::value>(f, As, Bs, h, wm, wn, lane);
+    };
+    auto mfma_op = [&](ACC &acc, const FR &f, auto q_c) {
+        mfma_one16<TM, TN, decltype(q_c)::value>(acc, f);
+    };
 
     // One half stage (as in gemm_dma_tile): the MFMAs of `cur`, the fragment
     // reads of the next half into `nxt` (READS), and in half 1 the loads of
@@ -250,7 +320,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
         Group grp;
         static_for<NMF>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
-            mfma_one_t<TM, TN, q>(acc, cur);
+            mfma_op(acc, cur, std::integral_constant<int, q>{});
             constexpr int cnt = (q + 1) * NOPS / NMF - q * NOPS / NMF;
             static_for<cnt>([&](auto oc) {
                 constexpr int o = q * NOPS / NMF + decltype(oc)::value;
@@ -261,8 +331,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
                         grp = dma_prep(S + 2, lsd, some, li / G, mode_c);
                     issue(grp, std::integral_constant<int, li % G>{});
                 } else if constexpr (READS) {
-                    read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, rd>(nxt, An, Bn, 1 - H, wm, wn,
-                                                                    lane);
+                    read_op(nxt, An, Bn, 1 - H, std::integral_constant<int, rd>{});
                 }
             });
             __builtin_amdgcn_sched_barrier(0);
@@ -279,7 +348,6 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
     // Tile (m0, n0), tile number k, from the accumulators.  Staging rows are
     // 128 bytes (64 columns); 16-byte chunk c of row r sits at c ^ swz(r).
     auto epilogue = [&](ACC &acc, int64_t m0, int64_t n0, int k) {
-        const int r = lane & 31, hl = lane >> 5;
         if (scale) {
             // g - 1 = (m - n) / n of the wave's columns 2 lane, 2 lane + 1
             const float *mn = mn_area(k) + wn * WTN + 2 * lane;
@@ -288,29 +356,34 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
             *reinterpret_cast<float2 *>(gm1 + 2 * lane) =
                 make_float2((mv.x - nv.x) / nv.x, (mv.y - nv.y) / nv.y);
         }
+        const int q4 = lane >> 4;
+        // slab (i, hf): rows 32 i .. 32 i + 31 and columns 64 hf .. 64 hf + 63
+        // of the wave tile, accumulator blocks (2 i + ii, 4 hf + jj)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < WTM / 32; ++i) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int j = 2 * hf + jj;
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int rr = 16 * ii + (lane & 15);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    for (int jj = 0; jj < 4; ++jj) {
                         float v[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            v[e] = g.alpha * acc[i][j][4 * q + e];
+                            v[e] = g.alpha * acc[2 * i + ii][4 * hf + jj][e];
                         if (scale) {
-                            const float4 f =
-                                *reinterpret_cast<const float4 *>(gm1 + j * 32 + 8 * q + 4 * hl);
+                            const float4 f = *reinterpret_cast<const float4 *>(
+                                gm1 + hf * 64 + 16 * jj + 4 * q4);
                             v[0] = __fmaf_rn(f.x, v[0], v[0]);
                             v[1] = __fmaf_rn(f.y, v[1], v[1]);
                             v[2] = __fmaf_rn(f.z, v[2], v[2]);
                             v[3] = __fmaf_rn(f.w, v[3], v[3]);
                         }
-                        const int c = jj * 4 + q;
-                        *reinterpret_cast<uint2 *>(stg + r * 128 + ((c ^ swz(r)) << 4) + 8 * hl) =
+                        // columns 16 jj + 4 q4 .. + 3: bytes 32 jj + 8 q4 of the row
+                        const int c = 2 * jj + (q4 >> 1);
+                        *reinterpret_cast<uint2 *>(stg + rr * 128 + ((c ^ swz(rr)) << 4) +
+                                                   8 * (q4 & 1)) =
                             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                     }
                 }
@@ -359,23 +432,20 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
     }
     wait_vmcnt<C::LPS>();
     stage_barrier();
-    static_for<NRD>([&](auto oc) {
-        read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, decltype(oc)::value>(
-            fa, slot(0), slot(0) + C::A_BYTES, 0, wm, wn, lane);
-    });
+    static_for<NRD>([&](auto oc) { read_op(fa, slot(0), slot(0) + C::A_BYTES, 0, oc); });
 
     int64_t S0 = 0;  // running index of the current tile's stage 0
 #pragma unroll 1
     for (int k = 0; k < count; ++k) {
         const int L = first + k * per;
         const bool has_next = k + 1 < count;
-        f32x16_t acc[TM][TN];
+        ACC acc;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
+                for (int v = 0; v < 4; ++v)
                     acc[i][j][v] = 0.f;
         auto stages = [&](int64_t D0, int64_t D1, auto mode_c) {
 #pragma unroll 1
@@ -388,11 +458,25 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
         };
         if (0 < b1)
             use_plan(0, L);
-        stages(0, e0, std::integral_constant<int, LOAD_SEG0>{});
-        stages(e0, b1, std::integral_constant<int, LOAD_ANY>{});
+        // the tile's first stage outside the stage loops: entered from the
+        // zeroed accumulators, the loops' 64 four-register accumulators were
+        // otherwise given other registers than the ones they leave in, and
+        // copied back every stage
+        int64_t D0 = 0;
+        if (dd >= 1) {
+            if (b1 == 0)
+                use_plan(1, L);  // its loads (stage 2) lie in segment 1
+            half(acc, std::integral_constant<int, 0>{}, S0, 2, true, fa, fb,
+                 std::integral_constant<int, LOAD_ANY>{}, std::true_type{}, -1, 0);
+            half(acc, std::integral_constant<int, 1>{}, S0, 2, true, fb, fa,
+                 std::integral_constant<int, LOAD_ANY>{}, std::true_type{}, -1, 0);
+            D0 = 1;
+        }
+        stages(std::min(D0, e0), e0, std::integral_constant<int, LOAD_SEG0>{});
+        stages(std::max(D0, e0), b1, std::integral_constant<int, LOAD_ANY>{});
         use_plan(1, L);
-        stages(b1, e1, std::integral_constant<int, LOAD_SEG1>{});
-        stages(e1, dd, std::integral_constant<int, LOAD_ANY>{});
+        stages(std::max(D0, b1), e1, std::integral_constant<int, LOAD_SEG1>{});
+        stages(std::max(D0, e1), dd, std::integral_constant<int, LOAD_ANY>{});
         // the last two stages load the next tile's stages 0 and 1 (the last
         // tile's load nothing: branch-free, with empty descriptor ranges)
         const int nxt = has_next ? L + per : L;
@@ -424,10 +508,7 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_dma_persistent_kernel(G
         S0 += nst;
         // the first fragments of the next tile (its stage 0 has landed: the
         // last half waited for it)
-        static_for<NRD>([&](auto oc) {
-            read_one<AK, BKM, BM, BN, TM, TN, WTM, WTN, decltype(oc)::value>(
-                fa, slot(S0), slot(S0) + C::A_BYTES, 0, wm, wn, lane);
-        });
+        static_for<NRD>([&](auto oc) { read_op(fa, slot(S0), slot(S0) + C::A_BYTES, 0, oc); });
     }
     wait_vmcnt<0>();  // the last tile's empty loads have deposited their zeros
 }
