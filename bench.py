@@ -26,8 +26,8 @@ Printed JSON line (one):
                traffic_ratio that over the algorithmic bytes.
   norm_*       dora_factored_norm alone: algorithmic flops (U, G, B G once,
                the row sums and dots) / time against the 2.5 PFLOP/s dense
-               bf16 peak; norm_kernels_us its five kernels from the
-               profiler's device trace; norm_U_mfma_util U = W A^T alone.
+               bf16 peak; norm_kernels_us its kernels from the profiler's
+               device trace; norm_U_mfma_util U = W A^T alone.
   fwd_cached_norm_us  dora_forward with the norm given (n_in), as inference
                with frozen adapters runs it.
   compose_*    dora_compose alone on the workload's [T, d_out], HBM GB/s
@@ -77,6 +77,8 @@ GROUP_LAYERS = 8   # decoder layers whose 7 projections form the grouped-norm wo
 CONFIGS = ("c2", "c3", "c4", "c5")
 NORM_KERNELS = ("gram_AAt", "gram_finalize", "U_WAt_rowdot", "BG_rowdot", "finish")
 NORM_KERNELS_G_IN_U = ("U_WAt_rowdot", "BG_rowdot", "finish")  # G's tiles beside U's
+# G's split-K tiles in U's split launch, then G's finalize
+NORM_KERNELS_G_SPLIT_IN_U = ("U_WAt_rowdot", "gram_finalize", "BG_rowdot", "finish")
 
 
 def log(*a):
@@ -201,10 +203,12 @@ def short_name(name):
 def norm_split(torch, fn, calls=5):
     """The factored norm's kernels averaged over `calls` calls: five (G =
     A A^T, its finalize, U = W A^T with the row sums and dots, B G with the
-    row dots, the finish), or three where G's tiles run in U's launch (U and
-    G together, B G, the finish); None if the trace shows neither."""
+    row dots, the finish); three where G's tiles run unsplit in U's launch
+    (U and G together, B G, the finish); or four where G's split tiles run
+    in U's split launch (U and G, G's finalize, B G, the finish).  None if
+    the trace shows none of these."""
     ks = device_kernels(torch, fn, calls)
-    for names in (NORM_KERNELS, NORM_KERNELS_G_IN_U):
+    for names in (NORM_KERNELS, NORM_KERNELS_G_IN_U, NORM_KERNELS_G_SPLIT_IN_U):
         k = len(names)
         if len(ks) == k * calls:
             return {key: round(sum(ks[k * c + i][1] for c in range(calls)) / calls, 1)

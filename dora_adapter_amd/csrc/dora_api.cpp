@@ -231,6 +231,10 @@ struct NormPlan {
     // workgroups with room beside U's tiles, U unsplit): G's tiles take as
     // long as U's (the same K) and write G_hi / G_lo themselves
     bool g_with_u = false;
+    // G = A A^T as split-K tiles of a split U launch (split like U, fp32
+    // partials, then the fixed-order finalize), where both fit beside each
+    // other on the CUs
+    bool g_split_with_u = false;
     size_t o_gpart, o_gfin, o_base, o_cross, o_gram;
     size_t bytes;
 };
@@ -252,6 +256,18 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, Carve &cv)
         const int64_t tg = ((r + t.BM - 1) / t.BM) * ((r + t.BN - 1) / t.BN);
         if (tu + tg <= kCUs && dma_operand(r, d_in)) {
             p.g_with_u = true;
+            p.g = p.u;
+            p.g.ntn = static_cast<int>((r + t.BN - 1) / t.BN);
+        }
+    } else if (bf && p.u.splits > 1 && gemm_bf16_cfg(p.u.cfg).dma &&
+               gemm_bf16_cfg(p.u.cfg).store_ok && dma_operand(r, d_in)) {
+        // workgroups resident per CU: two stage slots of both operand tiles
+        const TileCfg t = gemm_bf16_cfg(p.u.cfg);
+        const int64_t per_cu = (160 * 1024) / (2 * (t.BM + t.BN) * GEMM_DMA_BK * 2);
+        const int64_t tu = ((d_out + t.BM - 1) / t.BM) * ((r + t.BN - 1) / t.BN);
+        const int64_t tg = ((r + t.BM - 1) / t.BM) * ((r + t.BN - 1) / t.BN);
+        if ((tu + tg) * p.u.splits <= kCUs * per_cu) {
+            p.g_split_with_u = true;
             p.g = p.u;
             p.g.ntn = static_cast<int>((r + t.BN - 1) / t.BN);
         }
@@ -673,8 +689,14 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
     } else {
         gg.out = gpart;
         gg.out_f32 = 1;
-        DORA_LAUNCH(run_gemm(bf, p.g, gg, 0, false, st), "gram A A^T");
-        DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, gfin, st), "gram finalize");
+        if (p.g_split_with_u) {
+            gg.splits = p.g.splits;
+            gg.steps_per_split = p.g.sps;
+        } else {
+            DORA_LAUNCH(run_gemm(bf, p.g, gg, 0, false, st), "gram A A^T");
+            DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, gfin, st),
+                        "gram finalize");
+        }
     }
     // U = W A^T never leaves the tile: cross partials = rowdot(U_tile, B_tile),
     // base partials = row sums of W^2 from the same staged W.
@@ -690,7 +712,7 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
             g.out = U_out;
             g.ldc = r;
         }
-        if (p.g_with_u) {
+        if (p.g_with_u || p.g_split_with_u) {
             // one launch: U's tiles, then G's
             GemmGroup grp;
             memset(&grp, 0, sizeof grp);
@@ -700,6 +722,9 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
             grp.p[0].steps_per_split = p.u.sps;
             grp.p[1] = gg;
             DORA_LAUNCH(launch_gemm_bf16_grouped(grp, 0, p.u.cfg, true, st), "cross W A^T, gram A A^T");
+            if (p.g_split_with_u)
+                DORA_LAUNCH(launch_gram_finalize(bf, gpart, p.g.splits, r, gfin, st),
+                            "gram finalize");
         } else {
             DORA_LAUNCH(run_gemm(bf, p.u, g, 0, true, st), "cross W A^T");
         }

@@ -400,13 +400,22 @@ __device__ __forceinline__ void norm_finish_row(int64_t i, const float *__restri
                                                 int64_t d_out, float s, float *__restrict__ n,
                                                 float *base, float *cross, float *gram)
 {
-    double b = 0.0, c = 0.0, g = 0.0;
-    for (int z = 0; z < zb; ++z)
-        b += bp[static_cast<int64_t>(z) * d_out + i];
-    for (int z = 0; z < zc; ++z)
-        c += cp[static_cast<int64_t>(z) * d_out + i];
-    for (int z = 0; z < zg; ++z)
-        g += gp[static_cast<int64_t>(z) * d_out + i];
+    // each sum in order z = 0, 1, ...; the loads of eight partials go out
+    // together (a missing one adds +0.0, which changes no sum)
+    auto sum = [&](const float *__restrict__ p, int nz) {
+        double acc = 0.0;
+        for (int z0 = 0; z0 < nz; z0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                v[q] = z0 + q < nz ? p[static_cast<int64_t>(z0 + q) * d_out + i] : 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc += v[q];
+        }
+        return acc;
+    };
+    const double b = sum(bp, zb), c = sum(cp, zc), g = sum(gp, zg);
     const double sd = static_cast<double>(s);
     double n2 = b + 2.0 * sd * c + sd * sd * g;
     if (n2 < 0.0)

@@ -358,7 +358,10 @@ constexpr TileCfg kCfgs[] = {
     // 4 waves (2 x 2), 128 x 128 per wave
     {256, 256, GEMM_DMA_BK, true, 1.00f, true, false, false, false, false},
     {256, 128, GEMM_DMA_BK, true, 0.80f, true, false, false, false, false},  // 4 waves (2 x 2)
-    {128, 128, GEMM_DMA_BK, true, 0.60f, true, false, false, false, false},  // 4 waves (2 x 2), 2 per CU
+    // 4 waves (2 x 2), 2 per CU; row sums of squares and row dots from the
+    // accumulators (the factored norm at small rank: N = r <= 128 fills the
+    // tile, where the rank-384 tiles would stage and multiply zeros)
+    {128, 128, GEMM_DMA_BK, true, 0.60f, true, true, true, false, false},
     // 4 waves (1 x 4): a whole rank-384 row block per tile, so the row-dot
     // products of the factored norm read W once, and products with N = r
     // (x A^T, dh B) read their long operand once

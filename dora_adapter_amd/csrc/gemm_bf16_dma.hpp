@@ -136,7 +136,9 @@ struct DmaCfg {
     static_assert(BN % EB == 0, "epilogue column slabs");
     // the staged row-dot epilogue needs whole wave rows and one slab; other
     // tiles form their row dots from the accumulators directly
-    static constexpr bool DIRECT_ROWDOT = ER != WTM_ || EB != BN;
+    // (and 128 x 128 tiles, the small-rank norm's: their row dots then need
+    // no LDS pass per wave row)
+    static constexpr bool DIRECT_ROWDOT = ER != WTM_ || EB != BN || (BM == 128 && BN == 128);
     // row-dot epilogue: the E tile (bf16, padded rows) and one partial sum
     // per wave column and tile row
     static constexpr int EP = BN * 2 + 16;

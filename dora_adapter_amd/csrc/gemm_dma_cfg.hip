@@ -43,6 +43,10 @@ template __global__ void dma::gemm_bf16_dma_persistent_kernel<256, 256, 2, 2, fa
 DORA_DMA_CONFIG(256, 128, 2, 2)
 #elif DORA_DMA_CFG == 2
 DORA_DMA_CONFIG(128, 128, 2, 2)
+// with the row sums of squares too (the norm's U = W A^T at small rank)
+template __global__ void dma::gemm_bf16_dma_kernel<128, 128, 2, 2, true, true, true>(GemmArgs);
+template __global__ void dma::gemm_bf16_dma_grouped_kernel<128, 128, 2, 2, true, true, true>(
+    GemmGroup);
 #elif DORA_DMA_CFG == 3
 // the 1 x 4 layout also sums the squares of A's rows (the norm's base term);
 // those two kernels compile in a unit of their own (DORA_DMA_CFG 5)

@@ -80,7 +80,7 @@ hipError_t launch_dma_layout(const GemmArgs &a, int layout, bool rowsq, hipStrea
     switch (layout) {
     case 0:
         if (rowsq) {
-            if constexpr (BM == 128 && BN == 384)
+            if constexpr (BM == 128 && (BN == 384 || BN == 128))
                 return launch_dma<BM, BN, WM, WN, true, true, true>(a, st);
             else
                 return hipErrorInvalidValue;
@@ -120,7 +120,7 @@ hipError_t launch_dma_group_layout(GemmGroup &g, int layout, bool rowsq, hipStre
     switch (layout) {
     case 0:
         if (rowsq) {
-            if constexpr (BM == 128 && BN == 384)
+            if constexpr (BM == 128 && (BN == 384 || BN == 128))
                 return launch_dma_group<BM, BN, WM, WN, true, true, true>(g, st);
             else
                 return hipErrorInvalidValue;
