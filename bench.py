@@ -131,12 +131,13 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-full", action="store_true",
                     help="time the oracle on the whole problem instead of a token sample")
     ap.add_argument("--leg", choices=["all", "step", "kernels", "base", "norm", "compose",
-                                      "stream", "copy"],
+                                      "stream", "copy", "groupnorm"],
                     default="all",
                     help="'base' launches only the dominant kernel, 'norm' only "
                          "dora_factored_norm, 'compose' only dora_compose, 'stream' only the "
                          "stream-ceiling kernel (for counter runs); 'copy' a plain device copy "
-                         "of known size (counter calibration)")
+                         "of known size (counter calibration); 'groupnorm' only the grouped "
+                         "norm of the 56-module decoder set")
     ap.add_argument("--iters", type=int, default=10, help="launches per kernel-leg timing")
     return ap.parse_args(argv)
 
@@ -270,6 +271,22 @@ def main(argv=None):
     sh0 = shapes[0]
     T = sh0.T
     timer = Timer(torch, args.iters)
+
+    if args.leg == "groupnorm":
+        r = sh0.r
+        group = synth.make_group(synth.decoder_layer_shapes() * GROUP_LAYERS, r, seed=5,
+                                 device=dev)
+        gm = [(g["W"], g["A"], g["B"], g["m"], g["s"]) for g in group]
+        ns_g = [torch.empty(W.shape[0], dtype=torch.float32, device=dev) for W, *_ in gm]
+        ws_g = D._ws(D.dora_factored_norm_grouped_workspace(gm, 1), dev)
+        for _ in range(KERNEL_WARMUP + args.iters):
+            D.dora_factored_norm_grouped(gm, ns=ns_g, ws=ws_g)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "groupnorm", "modules": len(gm),
+                          "launches": KERNEL_WARMUP + args.iters,
+                          "flops_per_launch": sum(norm_flops(W.shape[0], W.shape[1], r)
+                                                  for W, *_ in gm)}))
+        return
 
     if args.leg == "copy":
         nbytes = 1 << 30
