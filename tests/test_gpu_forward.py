@@ -42,6 +42,7 @@ def test_tiny_fp32_module():
     (1, 512, 384, 384, 1.0),
     (513, 384, 2048, 128, 0.5),
     (64, 512, 4008, 40, 1.0),  # few tiles: split-K across both K segments, ragged tails
+    (520, 1288, 2056, 96, 1.0),  # small-rank norm on 128 x 128 tiles, G in U's launch
 ])
 def test_bf16_matches_oracle(T, d_out, d_in, r, s):
     say("forward bf16", T, d_out, d_in, r)

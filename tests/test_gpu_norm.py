@@ -31,6 +31,10 @@ def _terms_ok(out, ref, s, dtype, what):
     (600, 1032, 40, torch.bfloat16, 2.0),
     (1000, 2048, 384, torch.bfloat16, 1.0),  # full rank-384 tile set, ragged d_out
     (520, 4096, 64, torch.bfloat16, 2.0),
+    # small ranks on the 128 x 128 row-dot tiles, split over K with G's split
+    # tiles in U's launch: a full tile width, a ragged one, a ragged d_out
+    (2048, 3072, 128, torch.bfloat16, 1.0),
+    (1288, 2056, 96, torch.bfloat16, 0.5),
 ])
 def test_norm_matches_oracle(d_out, d_in, r, dtype, s):
     say("norm", d_out, d_in, r, dtype)
