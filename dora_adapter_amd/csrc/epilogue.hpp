@@ -113,9 +113,13 @@ __device__ __forceinline__ void store_row8(float *o, const float (&v)[8], int cn
 // tid / (BN / 8) + k * NT / (BN / 8): per-column factors are loaded once, and
 // all row-dot operands are loaded before any is used, so their latencies
 // overlap.
+//
+// EPI_MERGE with `pre` set: the thread's ITER chunks of E were loaded before
+// (merge_chunk_load, same rows and columns), so no load waits here.
 template <int R, int BN, int CST, int NT, typename TE>
 __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g, int64_t mrow0,
-                                              int64_t n0, int z, int tn, int tid)
+                                              int64_t n0, int z, int tn, int tid,
+                                              const EChunk<TE> *pre = nullptr)
 {
     constexpr int CPR = BN / 8;  // 8-column chunks per row
     static_assert(BN % 8 == 0 && 64 % CPR == 0, "row chunks must tile a wavefront");
@@ -189,7 +193,9 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
         for (int it = 0; it < ITER; ++it) {
             const int64_t m = mrow0 + row0 + it * RSTEP;
             const bool live = m < M && cnt > 0;
-            if (live)
+            if (pre != nullptr)
+                e[it] = pre[it];
+            else if (live)
                 e[it].load(E + m * g.lde + n, cnt);
             else
                 e[it].zero();
@@ -247,6 +253,27 @@ __device__ __forceinline__ void epilogue_rows(const float *Cs, const GemmArgs &g
             if (c == 0 && m < M)
                 g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * M + m] = sum;
         }
+    }
+}
+
+// The E chunks epilogue_rows<R, BN, CST, NT> takes for thread tid on rows
+// [mrow0, mrow0 + R) from column n0 (EPI_MERGE: W's tile, loaded early).
+template <int R, int BN, int NT, typename TE>
+__device__ __forceinline__ void merge_chunk_load(EChunk<TE> *e, const GemmArgs &g, int64_t mrow0,
+                                                 int64_t n0, int tid)
+{
+    constexpr int CPR = BN / 8, ITER = R * CPR / NT, RSTEP = NT / CPR;
+    const int c = tid % CPR, row0 = tid / CPR;
+    const int64_t n = n0 + c * 8;
+    const int cnt = n >= g.N ? 0 : ((g.N - n) < 8 ? static_cast<int>(g.N - n) : 8);
+    const TE *E = static_cast<const TE *>(g.E);
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int64_t m = mrow0 + row0 + it * RSTEP;
+        if (m < g.M && cnt > 0)
+            e[it].load(E + m * g.lde + n, cnt);
+        else
+            e[it].zero();
     }
 }
 

@@ -704,6 +704,33 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
     };
 
     FR fa, fb;  // half 0 and half 1 of a stage
+    // EPI_MERGE on tiles of at most 128 x 128 (8 chunks, 32 VGPRs a thread):
+    // the thread's chunks of W's tile are loaded before the K loop, in the
+    // order the epilogue takes them, so their memory latency runs under the
+    // product instead of after it.  They are older than every stage load, so
+    // the stage waits below cover them too.
+    constexpr int MCPR = C::EB / 8;
+    constexpr int MITER = C::ER * MCPR / NT;
+    constexpr int NPASS_ = WTM / C::ER;
+    constexpr bool MPRE = C::DIRECT_ROWDOT && !DH && !ROWSQ && BM * BN <= 128 * 128;
+    EChunk<uint16_t> wpre[MPRE ? WM * NPASS_ * (BN / C::EB) * MITER : 1];
+    const bool mpre = MPRE && g.mode == EPI_MERGE;
+    if constexpr (MPRE) {
+        if (mpre) {
+            static_for<WM>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                static_for<NPASS_>([&](auto pc) {
+                    constexpr int pass = decltype(pc)::value;
+                    static_for<BN / C::EB>([&](auto sc) {
+                        constexpr int sl = decltype(sc)::value;
+                        constexpr int at = ((h * NPASS_ + pass) * (BN / C::EB) + sl) * MITER;
+                        merge_chunk_load<C::ER, C::EB, NT, uint16_t>(
+                            wpre + at, g, m0 + h * WTM + pass * C::ER, n0 + sl * C::EB, tid);
+                    });
+                });
+            });
+        }
+    }
     if (s_begin < s_end) {
         // prologue: stages s_begin and s_begin + 1 in flight, then s_begin
         // visible and the fragments of its half 0 read
@@ -899,8 +926,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
             // ER rows of a wave row at a time: that wave stages them in LDS,
             // then every thread stores (or merges) them, EB columns per call
             constexpr int NPASS = WTM / C::ER, TMP = C::ER / 32;
-#pragma unroll 1
-            for (int h = 0; h < WM; ++h) {
+            static_for<WM>([&](auto hc) __attribute__((always_inline)) {
+                constexpr int h = decltype(hc)::value;
                 static_for<NPASS>([&](auto pc) __attribute__((always_inline)) {
                     constexpr int pass = decltype(pc)::value;
                     if (wm == h) {
@@ -919,13 +946,15 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                     __syncthreads();
                     static_for<BN / C::EB>([&](auto sc) __attribute__((always_inline)) {
                         constexpr int sl = decltype(sc)::value;
+                        constexpr int at = MPRE ? ((h * NPASS + pass) * (BN / C::EB) + sl) * MITER
+                                                : 0;
                         epilogue_rows<C::ER, C::EB, C::CST, NT, uint16_t>(
                             Cs + sl * C::EB, g, m0 + h * WTM + pass * C::ER, n0 + sl * C::EB, z,
-                            tn, tid);
+                            tn, tid, mpre ? wpre + at : nullptr);
                     });
                     __syncthreads();
                 });
-            }
+            });
         }
     } else {
         // a wave row at a time: that wave stages its rows in LDS, then every
