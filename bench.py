@@ -75,10 +75,10 @@ STREAM_LIB = os.path.join(ROOT, "dora_adapter_amd", "libstreamceil.so")
 KERNEL_WARMUP = 10  # untimed launches before each kernel-leg burst (the clock settles)
 GROUP_LAYERS = 8   # decoder layers whose 7 projections form the grouped-norm workload
 CONFIGS = ("c2", "c3", "c4", "c5")
-NORM_KERNELS = ("gram_AAt", "gram_finalize", "U_WAt_rowdot", "BG_rowdot", "finish")
-NORM_KERNELS_G_IN_U = ("U_WAt_rowdot", "BG_rowdot", "finish")  # G's tiles beside U's
-# G's split-K tiles in U's split launch, then G's finalize
-NORM_KERNELS_G_SPLIT_IN_U = ("U_WAt_rowdot", "gram_finalize", "BG_rowdot", "finish")
+# The factored norm's kernels, by role: G = A A^T, its finalize into the
+# bf16 hi / lo pair, U = W A^T (with G's tiles where they ride in its launch),
+# B G, and the finish (absent where B G's epilogue forms n)
+NORM_ROLES = ("gram_AAt", "gram_finalize", "U_WAt_rowdot", "BG_rowdot", "finish")
 
 
 def log(*a):
@@ -202,19 +202,33 @@ def short_name(name):
 
 
 def norm_split(torch, fn, calls=5):
-    """The factored norm's kernels averaged over `calls` calls: five (G =
-    A A^T, its finalize, U = W A^T with the row sums and dots, B G with the
-    row dots, the finish); three where G's tiles run unsplit in U's launch
-    (U and G together, B G, the finish); or four where G's split tiles run
-    in U's split launch (U and G, G's finalize, B G, the finish).  None if
-    the trace shows none of these."""
+    """The factored norm's kernels averaged over `calls` calls, keyed by role
+    (NORM_ROLES): the finalize and finish kernels by name, the products in
+    launch order (G, U, B G when G has a launch of its own; U, B G when G's
+    tiles ride in U's launch).  None if the trace does not split into calls
+    of that form."""
     ks = device_kernels(torch, fn, calls)
-    for names in (NORM_KERNELS, NORM_KERNELS_G_IN_U, NORM_KERNELS_G_SPLIT_IN_U):
-        k = len(names)
-        if len(ks) == k * calls:
-            return {key: round(sum(ks[k * c + i][1] for c in range(calls)) / calls, 1)
-                    for i, key in enumerate(names)}
-    return None
+    if not ks or len(ks) % calls:
+        return None
+    k = len(ks) // calls
+    per = [ks[c * k:(c + 1) * k] for c in range(calls)]
+    names = [n for n, _ in per[0]]
+    prods = [i for i, n in enumerate(names) if "finalize" not in n and "norm_finish" not in n]
+    roles = {}
+    for i, n in enumerate(names):
+        if "finalize" in n:
+            roles[i] = "gram_finalize"
+        elif "norm_finish" in n:
+            roles[i] = "finish"
+    if len(prods) == 3:
+        roles.update(zip(prods, ("gram_AAt", "U_WAt_rowdot", "BG_rowdot")))
+    elif len(prods) == 2:
+        roles.update(zip(prods, ("U_WAt_rowdot", "BG_rowdot")))
+    else:
+        return None
+    if any([n for n, _ in p] != names for p in per):
+        return None
+    return {roles[i]: round(sum(p[i][1] for p in per) / calls, 1) for i in range(k)}
 
 
 class StreamCeiling:

@@ -673,6 +673,12 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
     float *bpart = reinterpret_cast<float *>(ws + p.o_base);
     float *cpart = reinterpret_cast<float *>(ws + p.o_cross);
     float *gmpart = reinterpret_cast<float *>(ws + p.o_gram);
+    // the finish rides in B G's epilogue where that product is unsplit with
+    // one N tile on a kernel whose row dots come from the accumulators (and
+    // the separate terms are not asked for)
+    const bool fuse_finish = bf && base == nullptr && cross == nullptr && gram == nullptr &&
+                             p.bg.splits == 1 && p.bg.ntn == 1 && p.u.ntn == 1 &&
+                             gemm_bf16_cfg(p.bg.cfg).dma && gemm_bf16_cfg(p.bg.cfg).direct_rowdot;
 
     // G = A A^T, split-K partials, then a fixed-order sum (+ hi/lo split for
     // bf16); or, beside U's tiles, unsplit tiles writing G_hi and G_lo.
@@ -762,6 +768,15 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
             g.out_accum = 1;
             g.alpha = s;
         }
+        if (fuse_finish) {
+            // the whole Gram term is this product's row dot: its epilogue
+            // also forms n (the finish kernel's arithmetic, same order)
+            g.fin_n = n;
+            g.fin_base = bpart;
+            g.fin_cross = cpart;
+            g.fin_z = p.u.splits;
+            g.fin_s = s;
+        }
         DORA_LAUNCH(run_gemm(bf, p.bg, g, 1, false, st), "gram B G");
         if (U_out && p.bg.splits > 1) {
             a.mode = EPI_STORE;
@@ -776,9 +791,11 @@ int norm_impl(const void *W, const void *A, const void *B, float s, int64_t d_ou
                         "V A^T += s B G");
         }
     }
-    DORA_LAUNCH(launch_norm_finish(bpart, p.u.splits, cpart, p.u.splits * p.u.ntn, gmpart,
-                                   p.bg.splits * p.bg.ntn, d_out, s, n, base, cross, gram, st),
-                "norm finish");
+    if (!fuse_finish)
+        DORA_LAUNCH(launch_norm_finish(bpart, p.u.splits, cpart, p.u.splits * p.u.ntn, gmpart,
+                                       p.bg.splits * p.bg.ntn, d_out, s, n, base, cross, gram,
+                                       st),
+                    "norm finish");
     return DORA_OK;
 }
 

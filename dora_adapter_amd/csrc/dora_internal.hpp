@@ -52,15 +52,36 @@ struct GemmArgs {
     // s P from one accumulator); with out2_lo (bf16 only) it receives instead
     // the rounding residual C - bf16(C) of the first output, rounded to bf16
     // (the Gram matrix's hi / lo pair)
-    void *out2;
-    float alpha2;
-    int out2_lo;
+    //
+    // EPI_ROWDOT on the direct-to-LDS kernels whose row dots come from the
+    // accumulators, unsplit and one N tile (the norm's B G, whose row dot is
+    // the whole Gram term): with fin_n set, the same fields instead carry the
+    // norm's finish, n[m] = norm_from_terms(sum_z fin_base[z M + m],
+    // sum_z fin_cross[z M + m], rowdot of row m, fin_s) over z < fin_z.
+    union {
+        void *out2;
+        float *fin_n;
+    };
+    union {
+        float alpha2;
+        float fin_s;
+    };
+    union {
+        int out2_lo;
+        int fin_z;
+    };
     // optional per-column magnitude scale of the store: with colm and coln
     // set, column n of alpha * C is stored as h + ((colm[n] - coln[n]) /
     // coln[n]) h, i.e. (m/n) h in the cancellation-safe form (EPI_MERGE:
     // per-row factors)
-    const float *colm;
-    const float *coln;
+    union {
+        const float *colm;
+        const float *fin_base;
+    };
+    union {
+        const float *coln;
+        const float *fin_cross;
+    };
     // EPI_ROWDOT, EPI_MERGE: E (ld lde); EPI_ROWDOT: rowdot; and an
     // optional sum of squares of A's rows over each split's K range (K-major
     // A only; written by the tiles of the first N block): rowsq[z*M + m].
@@ -83,6 +104,17 @@ struct GemmArgs {
     };
     const float *dh_m, *dh_n;
 };
+
+// n = sqrt(max(base + 2 s cross + s^2 gram, 0)) from the three terms of the
+// factored norm, in fp64 (the finish kernel and the fused B G epilogue).
+__device__ __forceinline__ float norm_from_terms(double b, double c, double g, float s)
+{
+    const double sd = static_cast<double>(s);
+    double n2 = b + 2.0 * sd * c + sd * sd * g;
+    if (n2 < 0.0)
+        n2 = 0.0;
+    return static_cast<float>(sqrt(n2));
+}
 
 // Up to kMaxGroup independent products in one launch (passed by value as the
 // kernel argument, so no descriptor table lives in device memory).  Every

@@ -416,11 +416,7 @@ __device__ __forceinline__ void norm_finish_row(int64_t i, const float *__restri
         return acc;
     };
     const double b = sum(bp, zb), c = sum(cp, zc), g = sum(gp, zg);
-    const double sd = static_cast<double>(s);
-    double n2 = b + 2.0 * sd * c + sd * sd * g;
-    if (n2 < 0.0)
-        n2 = 0.0;
-    n[i] = static_cast<float>(sqrt(n2));
+    n[i] = norm_from_terms(b, c, g, s);
     if (base)
         base[i] = static_cast<float>(b);
     if (cross)

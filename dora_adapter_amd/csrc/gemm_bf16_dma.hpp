@@ -919,8 +919,19 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmArgs &g, const int tm, c
                 float sum = 0.f;
                 for (int w = 0; w < WN; ++w)
                     sum += red[w * BM + r];
-                if (m0 + r < g.M)
-                    g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * g.M + m0 + r] = sum;
+                const int64_t m = m0 + r;
+                if (m < g.M) {
+                    g.rowdot[(static_cast<int64_t>(z) * ntn + tn) * g.M + m] = sum;
+                    if (g.fin_n != nullptr) {
+                        // the norm's finish: the partials summed in order z
+                        double b = 0.0, c = 0.0;
+                        for (int q = 0; q < g.fin_z; ++q) {
+                            b += g.fin_base[static_cast<int64_t>(q) * g.M + m];
+                            c += g.fin_cross[static_cast<int64_t>(q) * g.M + m];
+                        }
+                        g.fin_n[m] = norm_from_terms(b, c, static_cast<double>(sum), g.fin_s);
+                    }
+                }
             }
         } else {
             // ER rows of a wave row at a time: that wave stages them in LDS,
