@@ -1102,6 +1102,11 @@ int norm_group_impl(const dora_module *mods, const std::vector<int> &which, int 
         // XCD runs the longest-first order gives the first XCDs all the
         // longest products: 3.39 -> 2.88 ms on 56 decoder projections)
         gg.spread = gu.spread = gbg.spread = 1;
+        // B G's epilogue forms n when every B G of the chunk is unsplit with
+        // one N tile (as for one module: the finish launch then goes)
+        bool fuse = gemm_bf16_cfg(c.bg.cfg).direct_rowdot && c.bg.splits == 1;
+        for (int k = 0; k < cnt; ++k)
+            fuse = fuse && c.pbg[k].ntn == 1 && c.pu[k].ntn == 1;
         for (int k = 0; k < cnt; ++k) {
             const dora_module &md = mods[which[c.i0 + k]];
             const int64_t r = md.r, d_in = md.d_in, d_out = md.d_out;
@@ -1141,6 +1146,13 @@ int norm_group_impl(const dora_module *mods, const std::vector<int> &which, int 
             b.rowdot = gmpart;
             b.splits = c.pbg[k].splits;
             b.steps_per_split = c.pbg[k].sps;
+            if (fuse) {
+                b.fin_n = n[which[c.i0 + k]];
+                b.fin_base = bpart;
+                b.fin_cross = cpart;
+                b.fin_z = c.pu[k].splits;
+                b.fin_s = md.s;
+            }
             nf.it[k] = NormFinishItem{bpart,
                                       cpart,
                                       gmpart,
@@ -1155,7 +1167,8 @@ int norm_group_impl(const dora_module *mods, const std::vector<int> &which, int 
         DORA_LAUNCH(launch_gram_finalize_grouped(bf, fin, st), "grouped gram finalize");
         DORA_LAUNCH(launch_gemm_bf16_grouped(gu, 0, c.u.cfg, true, st), "grouped cross W A^T");
         DORA_LAUNCH(launch_gemm_bf16_grouped(gbg, 1, c.bg.cfg, false, st), "grouped gram B G");
-        DORA_LAUNCH(launch_norm_finish_grouped(nf, st), "grouped norm finish");
+        if (!fuse)
+            DORA_LAUNCH(launch_norm_finish_grouped(nf, st), "grouped norm finish");
     }
     return DORA_OK;
 }
