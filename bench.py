@@ -201,18 +201,11 @@ def short_name(name):
     return n.replace("unsigned short", "bf16")
 
 
-def norm_split(torch, fn, calls=5):
-    """The factored norm's kernels averaged over `calls` calls, keyed by role
-    (NORM_ROLES): the finalize and finish kernels by name, the products in
-    launch order (G, U, B G when G has a launch of its own; U, B G when G's
-    tiles ride in U's launch).  None if the trace does not split into calls
-    of that form."""
-    ks = device_kernels(torch, fn, calls)
-    if not ks or len(ks) % calls:
-        return None
-    k = len(ks) // calls
-    per = [ks[c * k:(c + 1) * k] for c in range(calls)]
-    names = [n for n, _ in per[0]]
+def norm_roles(names):
+    """Role (NORM_ROLES) of each kernel of one factored-norm call, from the
+    kernel names in launch order: the finalize and finish kernels by name,
+    the products by position (G, U, B G when G has a launch of its own; U,
+    B G when G's tiles ride in U's launch).  None for any other form."""
     prods = [i for i, n in enumerate(names) if "finalize" not in n and "norm_finish" not in n]
     roles = {}
     for i, n in enumerate(names):
@@ -226,7 +219,21 @@ def norm_split(torch, fn, calls=5):
         roles.update(zip(prods, ("U_WAt_rowdot", "BG_rowdot")))
     else:
         return None
-    if any([n for n, _ in p] != names for p in per):
+    return [roles[i] for i in range(len(names))]
+
+
+def norm_split(torch, fn, calls=5):
+    """The factored norm's kernels averaged over `calls` calls, keyed by role
+    (norm_roles).  None if the trace does not split into equal calls of a
+    known form."""
+    ks = device_kernels(torch, fn, calls)
+    if not ks or len(ks) % calls:
+        return None
+    k = len(ks) // calls
+    per = [ks[c * k:(c + 1) * k] for c in range(calls)]
+    names = [n for n, _ in per[0]]
+    roles = norm_roles(names)
+    if roles is None or any([n for n, _ in p] != names for p in per):
         return None
     return {roles[i]: round(sum(p[i][1] for p in per) / calls, 1) for i in range(k)}
 

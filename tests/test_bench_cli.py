@@ -68,3 +68,23 @@ def test_traffic_record_describes_the_base_product():
     writes = tr["write_size_kib_per_launch"] * 1024 * cal["bytes"] / 1024 / cal["write_size_kib"]
     assert abs(writes - 2 * T * d_out) <= 1e-3 * writes
     assert len(tr["kernel_source_hash"]) == 16
+
+
+def test_norm_roles_of_each_launch_form():
+    """The norm's kernels are told apart by name (finalize, finish) and by
+    position (the products): the five-launch form, G's tiles unsplit or
+    split in U's launch, and the finish inside B G's epilogue."""
+    g = "void dora::dma::gemm_bf16_dma_kernel<128, 384, 2, 4, true, true, false, false>(x)"
+    u = "void dora::dma::gemm_bf16_dma_grouped_kernel<128, 384, 2, 4, true, true, true>(x)"
+    bg = "void dora::dma::gemm_bf16_dma_kernel<128, 384, 2, 4, true, false, false, false>(x)"
+    fz = "dora::(anonymous namespace)::gram_finalize_kernel(float const*, int, long)"
+    fn = "dora::(anonymous namespace)::norm_finish_kernel(float const*, int)"
+    assert bench.norm_roles([g, fz, u, bg, fn]) == list(bench.NORM_ROLES)
+    assert bench.norm_roles([u, bg, fn]) == ["U_WAt_rowdot", "BG_rowdot", "finish"]
+    assert bench.norm_roles([u, fz, bg, fn]) == ["U_WAt_rowdot", "gram_finalize", "BG_rowdot",
+                                                 "finish"]
+    assert bench.norm_roles([u, bg]) == ["U_WAt_rowdot", "BG_rowdot"]
+    assert bench.norm_roles([u, fz, bg]) == ["U_WAt_rowdot", "gram_finalize", "BG_rowdot"]
+    assert bench.norm_roles([g, fz, u, bg]) == ["gram_AAt", "gram_finalize", "U_WAt_rowdot",
+                                                "BG_rowdot"]
+    assert bench.norm_roles([u]) is None
